@@ -1,0 +1,295 @@
+"""Indexer benchmark on one MI355X: keys scored per second for one whole indexer step
+(logits over every cached key, causal masks, per-row top-k) on a seeded synthetic
+workload, with the dominant kernel's roofline fraction and the CPU oracle beside it.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 2] [--no-cpu-baseline]
+
+Default workload: paged fp8 decode, 32 sequences, context lengths U[1024, 16384], 64
+heads, logits width 32768, top-2048. ``--config 1..5`` selects one of the five
+workloads. Inputs live in HBM before timing starts. Each timed step reads a different
+copy of the K cache (copies totalling more than 512 MB rotate), so the 256 MB
+Infinity Cache cannot hold a step's keys from the previous visit.
+
+Prints ONE JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense fp8, published
+FLUSH_BYTES = 512 * 2**20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------------------------
+# algorithmic work per launch
+# ------------------------------------------------------------------------------------
+def paged_work(wl, ends):
+    """(keys scored, bytes, flop) of one paged logits launch: K read once per sequence,
+    queries, weights, block-table entries, lengths, and the full-width logits written."""
+    D, H = wl.D, wl.H
+    per_key = D + 4 if wl.fmt == "fp8" else D // 2 + D // 32
+    per_q = D if wl.fmt == "fp8" else D // 2 + 4 * (D // 32) // 4  # MXFP4: packed bytes + one int32 of scales
+    seq_len = ends.reshape(wl.B, wl.next_n).max(axis=1)
+    kbytes = int(seq_len.sum()) * per_key
+    qbytes = wl.rows * H * per_q
+    wbytes = wl.rows * H * 4
+    btbytes = int(np.ceil(seq_len / wl.page_size).sum()) * 4
+    lbytes = wl.B * 4
+    obytes = wl.rows * wl.width * 4
+    keys = int(ends.sum())
+    flop = 2 * H * D * keys
+    return keys, kbytes + qbytes + wbytes + btbytes + lbytes + obytes, flop
+
+
+def contig_work(wl):
+    M, H, D, N = wl.M, wl.H, wl.D, wl.N
+    keys = int(np.clip(wl.ke - wl.ks, 0, None).sum())
+    nbytes = M * H * D + N * (D + 4) + 4 * M * H + 8 * M + 4 * M * N
+    return keys, nbytes, 2 * H * D * keys
+
+
+# ------------------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample)
+# ------------------------------------------------------------------------------------
+def cpu_baseline(cfg, wl, budget_s: float = 10.0):
+    """The CPU oracle (float64 NumPy, BLAS per head) on a bounded sample of the same
+    workload: whole sequences (paged) or blocks of query rows (contiguous), taken in
+    order until about ``budget_s`` seconds of logits + top-k work have run.
+    Quantisation of the sample's inputs is not timed."""
+    from oracle import cache, formats, indexer
+
+    threads = os.cpu_count()
+    try:
+        import threadpoolctl
+
+        blas = [i["num_threads"] for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            threads = max(blas)
+    except Exception:
+        pass
+    spent, keys, units = 0.0, 0, 0
+    if cfg in (1, 4):
+        kc, ks = formats.quantize_k_fp8(wl.k)
+        step = 256 if cfg == 4 else wl.M
+        for r0 in range(0, wl.M, step):
+            rows = np.arange(r0, min(wl.M, r0 + step))
+            q = formats.quantize_fp8_noscale(wl.q[rows])
+            t0 = time.perf_counter()
+            L = indexer.mqa_logits_fp8(q, kc, ks, wl.w[rows], wl.ks[rows], wl.ke[rows])
+            indexer.topk(L, wl.ks[rows], wl.ke[rows], wl.topk)
+            spent += time.perf_counter() - t0
+            keys += int(np.clip(wl.ke[rows] - wl.ks[rows], 0, None).sum())
+            units += len(rows)
+            if spent >= budget_s:
+                break
+        sample = f"query rows 0..{units - 1} of {wl.M} against all {wl.N} keys, logits + top-{wl.topk}"
+    else:
+        P, D = wl.page_size, wl.D
+        for b in range(wl.B):
+            kr = np.arange(wl.key_offsets[b], wl.key_offsets[b] + wl.context_lens[b])
+            rows = np.arange(b * wl.next_n, (b + 1) * wl.next_n)
+            if wl.fmt == "fp8":
+                pool = np.zeros((wl.num_pages, cache.fp8_page_bytes(P, D)), np.uint8)
+                codes, sc = formats.quantize_k_fp8(wl.k[kr])
+                cache.store_fp8(pool, wl.slot_mapping[kr], codes, sc, P)
+                q, qs = formats.quantize_fp8_noscale(wl.q[b:b + 1]), None
+            else:
+                pool = np.zeros((wl.num_pages, cache.mxfp4_page_bytes(P, D)), np.uint8)
+                packed, sb = formats.quantize_mxfp4(wl.k[kr])
+                cache.store_mxfp4(pool, wl.slot_mapping[kr], packed, sb, P)
+                q, qsb = formats.quantize_mxfp4(wl.q[b:b + 1])
+                qs = formats.scales_to_int32(qsb)
+            t0 = time.perf_counter()
+            L = indexer.paged_logits(pool, wl.fmt, P, wl.block_table[b:b + 1], wl.context_lens[b:b + 1], q,
+                                     wl.w[rows], 1, wl.next_n, wl.width, q_scale=qs)
+            ends = indexer.paged_row_ends(wl.context_lens[b:b + 1], 1, wl.next_n)
+            indexer.topk(L, None, ends, wl.topk)
+            spent += time.perf_counter() - t0
+            keys += int(ends.sum())
+            units += 1
+            if spent >= budget_s:
+                break
+        sample = f"sequences 0..{units - 1} of {wl.B} ({keys} row-keys), logits + top-{wl.topk}"
+    return {"value": round(keys / spent, 1), "unit": "keys/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "seconds": round(spent, 2)}
+
+
+# ------------------------------------------------------------------------------------
+# GPU
+# ------------------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the indexer path here has no multi-GPU mode (each GPU would "
+              "score its own sequences independently); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_attention_indexer_mxfp4_amd import ops, workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = args.config
+    wl = workloads.CONFIGS[cfg]()
+    paged = cfg in (2, 3, 5)
+
+    if paged:
+        fmt = ops.FP8 if wl.fmt == "fp8" else ops.MXFP4
+        pb = ops.page_bytes(fmt, wl.page_size)
+        copies = max(1, int(np.ceil(FLUSH_BYTES / (wl.num_pages * pb))))
+        k_dev = torch.from_numpy(wl.k).to(dev)
+        slots = torch.from_numpy(wl.slot_mapping).to(dev)
+        pools = []
+        for _ in range(copies):
+            pool = torch.zeros((wl.num_pages, pb), dtype=torch.uint8, device=dev)
+            ops.idx_k_store(pool, fmt, wl.page_size, k_dev, slots)  # quantise K with the library's own store
+            pools.append(pool)
+        # K store throughput (boundary op, timed on its own)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ops.idx_k_store(pools[0], fmt, wl.page_size, k_dev, slots)
+        e1.record()
+        torch.cuda.synchronize()
+        kstore_ms = e0.elapsed_time(e1)
+        del k_dev
+        q, q_scale = ops.idx_q_quant(torch.from_numpy(wl.q.reshape(-1, wl.H, wl.D)).to(dev), fmt)
+        q = q.view(wl.B, wl.next_n, wl.H, -1).contiguous()
+        if q_scale is not None:
+            q_scale = q_scale.view(wl.B, wl.next_n, wl.H).contiguous()
+        w = torch.from_numpy(wl.w).to(dev)
+        ctx = torch.from_numpy(wl.context_lens).to(dev)
+        bt = torch.from_numpy(wl.block_table).to(dev)
+        rows = wl.rows
+        logits = torch.empty((rows, (wl.width + 3) // 4 * 4), dtype=torch.float32, device=dev)[:, :wl.width]
+        ends = torch.empty(rows, dtype=torch.int32, device=dev)
+        out = torch.empty((rows, wl.topk), dtype=torch.int32, device=dev)
+
+        def logits_call(i):
+            ops.idx_paged_mqa_logits(pools[i % copies], fmt, wl.page_size, q, q_scale, w, ctx, bt, wl.width,
+                                     logits=logits, row_end_out=ends)
+
+        def topk_call():
+            ops.idx_topk(logits, None, ends, wl.topk, out=out)
+
+        ends_host = None
+    else:
+        fmt = ops.FP8
+        kq = torch.from_numpy(wl.k).to(dev)
+        copies = max(1, int(np.ceil(FLUSH_BYTES / (wl.N * (wl.D + 4)))))
+        qc, _ = ops.idx_q_quant(torch.from_numpy(wl.q).to(dev), fmt)
+        # contiguous K: quantise through a page-size-16 pool and view its bytes back as rows
+        P = 16
+        npages = (wl.N + P - 1) // P
+        kpools = []
+        for _ in range(copies):
+            pool = torch.zeros((npages, P * (wl.D + 4)), dtype=torch.uint8, device=dev)
+            ops.idx_k_store(pool, fmt, P, kq, torch.arange(wl.N, dtype=torch.int64, device=dev))
+            vals = pool[:, : P * wl.D].reshape(npages * P, wl.D)[: wl.N]
+            scal = pool[:, P * wl.D:].contiguous().view(torch.float32).reshape(-1)[: wl.N]
+            kpools.append((vals, scal.contiguous()))
+        kstore_ms = None
+        w = torch.from_numpy(wl.w).to(dev)
+        ks = torch.from_numpy(wl.ks).to(dev)
+        ke = torch.from_numpy(wl.ke).to(dev)
+        logits = torch.empty((wl.M, (wl.N + 3) // 4 * 4), dtype=torch.float32, device=dev)[:, :wl.N]
+        out = torch.empty((wl.M, wl.topk), dtype=torch.int32, device=dev)
+
+        def logits_call(i):
+            vals, scal = kpools[i % copies]
+            ops.idx_mqa_logits(qc, vals, scal, w, ks, ke, logits=logits)
+
+        def topk_call():
+            ops.idx_topk(logits, ks, ke, wl.topk, out=out)
+
+    # warmup
+    for i in range(args.warmup):
+        logits_call(i)
+        topk_call()
+    torch.cuda.synchronize()
+    if paged:
+        ends_host = ends.cpu().numpy()
+        keys, nbytes, flop = paged_work(wl, ends_host)
+    else:
+        keys, nbytes, flop = contig_work(wl)
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        a, b, c = ev[i]
+        a.record(stream)
+        logits_call(i)
+        b.record(stream)
+        topk_call()
+        c.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    logits_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    topk_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = keys * args.steps / elapsed
+    if cfg == 4 or cfg == 1:
+        achieved = flop / (logits_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP8_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "mqa_logits_fp8_kernel", "kernel_ms": round(logits_ms, 4),
+                "algorithmic_flop": flop, "algorithmic_bytes": nbytes}
+    else:
+        achieved = nbytes / (logits_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "paged_logits_kernel",
+                "kernel_ms": round(logits_ms, 4), "algorithmic_bytes": nbytes, "algorithmic_flop": flop}
+    result = {
+        "metric": "indexer keys scored/sec + decode HBM GB/s (% of peak), 1 MI355X",
+        "value": round(value, 1),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if wl_fmt(wl, cfg) == "fp8" else "fp4",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "config": cfg, "keys_per_step": keys, "topk": wl.topk,
+                   "logits_ms": round(logits_ms, 4), "topk_ms": round(topk_ms, 4),
+                   "kstore_ms": None if kstore_ms is None else round(kstore_ms, 4), "k_cache_copies": copies},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, wl)
+    print(json.dumps(result), flush=True)
+
+
+def wl_fmt(wl, cfg):
+    return getattr(wl, "fmt", "fp8")
+
+
+if __name__ == "__main__":
+    main()

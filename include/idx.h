@@ -1,0 +1,233 @@
+/*
+ * idx.h - C ABI of libidx, the sparse-attention indexer for MI355X (gfx950).
+ *
+ * The indexer scores every cached key s for every query row t,
+ *
+ *     I[t, s] = sum_h w[t, h] * ReLU( dequant(q[t, h, :]) . dequant(k[s, :]) ),
+ *
+ * writes -inf outside each row's valid range [start_t, end_t), and picks each
+ * row's top-k keys. The operation is the one the vLLM API pages state:
+ *   - page "vllm.v1.attention.ops.rocm_aiter_mla_sparse", functions
+ *     fp8_mqa_logits_torch / rocm_fp8_mqa_logits (contiguous fp8 chunk) and
+ *     rocm_fp8_paged_mqa_logits (paged fp8 decode and MTP);
+ *   - page "vllm.v1.attention.ops.rocm_paged_mxfp4_indexer", functions
+ *     rocm_mxfp4_sparse_attn_indexer (MXFP4 query and K cache) and _topk;
+ *   - page "vllm.models.deepseek_v41.amd.rocm", functions
+ *     rocm_mxfp4_indexer_k_store and rocm_mxfp4_indexer_q_quant (the K store and
+ *     the query quantiser that feed the cache and the query).
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument that names tensor data is DEVICE memory owned by the
+ *     caller; descriptors (idx_paged_cache) are host structs. The library
+ *     allocates nothing and keeps no state besides a per-device cache of the
+ *     device's properties.
+ *   - Each call enqueues its kernels on `stream` (NULL = the null stream) and
+ *     returns without synchronising the host. No call allocates, copies to the
+ *     host or waits, so every call may be captured in a HIP graph; grids depend
+ *     only on the arguments, never on device-resident values.
+ *   - Arguments the host can see (pointers, sizes, strides, alignments, enums,
+ *     workspace sizes) are checked before anything is launched; a failed check
+ *     returns an error and launches nothing. Values that live on the device
+ *     (lengths, block-table entries, slots) are trusted to be in range; the
+ *     kernels clamp every address they form so an out-of-range value yields
+ *     unspecified results for the rows it touches, never an out-of-bounds access.
+ *   - A call whose work is empty (no rows, no keys) returns IDX_OK and launches
+ *     nothing.
+ *   - The only device supported is gfx950; IDX_ERR_DEVICE otherwise.
+ */
+#ifndef IDX_H
+#define IDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IDX_ABI_VERSION 1
+
+typedef enum {
+  IDX_OK = 0,
+  IDX_ERR_NULL = 1,      /* a required pointer is NULL */
+  IDX_ERR_SHAPE = 2,     /* a size is negative or outside what the kernels support */
+  IDX_ERR_STRIDE = 3,    /* a stride or an alignment requirement is not met */
+  IDX_ERR_FORMAT = 4,    /* an enum argument holds an unknown value */
+  IDX_ERR_WORKSPACE = 5, /* the workspace is smaller than the matching *_workspace() query */
+  IDX_ERR_LAUNCH = 6,    /* a kernel launch failed (hipGetLastError after the launch) */
+  IDX_ERR_DEVICE = 7     /* no current HIP device, or it is not a gfx950 */
+} idx_status;
+
+/* Format of a paged K cache. */
+typedef enum {
+  /* e4m3 (OCP float8_e4m3fn) values plus one fp32 scale per key. A page of P keys
+   * holds P*D value bytes (key u at u*D) followed by P little-endian fp32 scales
+   * (key u at P*D + 4u): page "vllm.v1.attention.ops.rocm_aiter_mla_sparse",
+   * rocm_fp8_paged_mqa_logits and rocm_fp8_paged_mqa_logits_triton. */
+  IDX_KV_FP8_E4M3 = 0,
+  /* MXFP4: D/2 bytes of packed e2m1 (element 2i in the low nibble of byte i) and
+   * D/32 e8m0 scales (bias 127) per key. The page is cut into runs of 16 keys; in a
+   * run the packed bytes are stored [16-byte chunk, key, byte] and the scale bytes
+   * [scale % 4, key, scale / 4]. The value bytes of all runs come first, the scale
+   * bytes of all runs follow them: page
+   * "vllm.v1.attention.ops.rocm_paged_mxfp4_indexer", RocmPagedMxfp4CacheLayout and
+   * rocm_paged_mxfp4_cache_layout. */
+  IDX_KV_MXFP4_E2M1 = 1
+} idx_kv_format;
+
+/* Element type of full-precision rows handed to the quantisers. */
+typedef enum { IDX_IN_F32 = 0, IDX_IN_BF16 = 1 } idx_in_dtype;
+
+/* A paged K cache (host struct; `base` is device memory). Logical page p of
+ * sequence b is physical page block_table[b * block_table_stride + p]; key slot
+ * `slot` is entry slot % page_size of page slot / page_size. Page n starts at
+ * base + n * page_stride_bytes: the stride is the pool's and may exceed the page
+ * size (page "vllm.v1.attention.ops.rocm_paged_mxfp4_indexer", _kv_view). */
+typedef struct {
+  int32_t fmt;               /* idx_kv_format */
+  int32_t page_size;         /* keys per page P: a multiple of 16 in [16, 1024] */
+  int32_t num_pages;         /* pages in the pool, >= 1 */
+  int32_t head_dim;          /* D: must be 128 */
+  int64_t page_stride_bytes; /* >= bytes of one page, a multiple of 16 */
+  void *base;                /* device address of page 0, 16-byte aligned */
+} idx_paged_cache;
+
+/* Bytes one page of `fmt` needs: P*(D+4) for fp8, P*(D/2+D/32) for MXFP4; 0 for an
+ * unknown format. */
+size_t idx_page_bytes(int32_t fmt, int32_t page_size, int32_t head_dim);
+
+/*
+ * idx_mqa_logits - logits of a contiguous fp8 chunk (prefill).
+ * Page "vllm.v1.attention.ops.rocm_aiter_mla_sparse", fp8_mqa_logits_torch and
+ * rocm_fp8_mqa_logits.
+ *
+ *   q          [M, H, D] e4m3 bytes; row t starts at q + t*q_row_stride, head h of
+ *              it at + h*D. q_row_stride >= H*D and a multiple of 16 bytes.
+ *   k          [N, D] e4m3 bytes; key s at k + s*k_row_stride (multiple of 16, >= D).
+ *   k_scale    [N] fp32 per-key scales (> 0).
+ *   w          [M, H] fp32 head weights, row t at w + t*w_row_stride (elements,
+ *              >= H).
+ *   row_start  [M] int32, first valid key of row t (inclusive).
+ *   row_end    [M] int32, end of row t's valid keys (exclusive).
+ *   logits     [M, N] fp32 out, row t at logits + t*logits_row_stride (elements,
+ *              >= N, a multiple of 4; logits 16-byte aligned). Every column
+ *              0..N-1 of every row is written: I[t, s] on [row_start_t,
+ *              min(row_end_t, N)), -inf elsewhere.
+ *   Limits: D == 128, 1 <= H <= 128, M, N >= 0.
+ */
+idx_status idx_mqa_logits(const uint8_t *q, int64_t q_row_stride, const uint8_t *k, int64_t k_row_stride,
+                          const float *k_scale, const float *w, int64_t w_row_stride,
+                          const int32_t *row_start, const int32_t *row_end, int32_t M, int32_t N, int32_t H,
+                          int32_t D, float *logits, int64_t logits_row_stride, hipStream_t stream);
+
+/*
+ * idx_paged_mqa_logits - logits of a decode / MTP step over a paged K cache.
+ * Page "vllm.v1.attention.ops.rocm_aiter_mla_sparse", rocm_fp8_paged_mqa_logits
+ * (fp8); page "vllm.v1.attention.ops.rocm_paged_mxfp4_indexer",
+ * rocm_mxfp4_sparse_attn_indexer (MXFP4).
+ *
+ *   cache         the paged K cache (format, geometry, base).
+ *   q             fp8:   [B, next_n, H, D] e4m3 bytes, contiguous.
+ *                 MXFP4: [B, next_n, H, D/2] packed e2m1 bytes, contiguous.
+ *   q_scale       MXFP4: [B, next_n, H] int32, one per head holding its D/32 = 4
+ *                 e8m0 bytes, byte j (little-endian) for elements 32j..32j+31.
+ *                 Must be NULL for fp8 (the fp8 query carries no scale).
+ *   w             [B*next_n, H] fp32, contiguous; the softmax and head scales are
+ *                 already folded in.
+ *   context_lens  ctx_per_row == 0: [B] keys each sequence holds; row
+ *                 r = b*next_n + j is valid on [0, ctx_b - next_n + j + 1) (row j
+ *                 of a next_n-token verify sees its own token and those before it:
+ *                 page "vllm.v1.attention.backends.mla.rocm_aiter_mla",
+ *                 dcp_local_verify_row_lens).
+ *                 ctx_per_row != 0: [B*next_n], row r is valid on
+ *                 [0, context_lens[r]).
+ *                 Every end is clamped to [0, min(width, max_blocks*page_size)].
+ *   block_table   [B, max_blocks] int32, row b at block_table + b*block_table_stride.
+ *   logits        [B*next_n, width] fp32 out, row r at logits + r*logits_row_stride
+ *                 (elements, >= width, a multiple of 4; 16-byte aligned). Every
+ *                 column 0..width-1 is written (-inf past the row's end).
+ *   row_end_out   [B*next_n] int32 out, or NULL: each row's clamped end, ready to
+ *                 pass to idx_topk.
+ *   workspace     device scratch of at least idx_paged_mqa_logits_workspace()
+ *                 bytes (NULL when that is 0).
+ *   Limits: D == 128, 1 <= H <= 128, 1 <= next_n <= 4, 0 <= B <= 8192,
+ *   width >= 0.
+ */
+idx_status idx_paged_mqa_logits(const idx_paged_cache *cache, const void *q, const int32_t *q_scale,
+                                const float *w, const int32_t *context_lens, int32_t ctx_per_row,
+                                const int32_t *block_table, int64_t block_table_stride, int32_t max_blocks,
+                                int32_t B, int32_t next_n, int32_t H, float *logits, int64_t logits_row_stride,
+                                int32_t width, int32_t *row_end_out, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+size_t idx_paged_mqa_logits_workspace(int32_t B, int32_t next_n, int32_t H, const idx_paged_cache *cache);
+
+/*
+ * idx_topk - per-row top-k over [row_start, row_end).
+ * Page "vllm.v1.attention.ops.rocm_paged_mxfp4_indexer", _topk.
+ *
+ *   logits     [rows, width] fp32, row r at logits + r*logits_row_stride (elements).
+ *   row_start  [rows] int32 or NULL (all 0); row_end [rows] int32. Both are clamped
+ *              to [0, width].
+ *   out        [rows, k] int32, row r at out + r*out_row_stride (elements, >= k).
+ *              Row r receives the columns of its min(k, end - start) largest
+ *              logits, as column - start, in ascending column order, then -1 up to
+ *              k entries. Ties at the k-th value go to the lowest column; -0.0 and
+ *              +0.0 compare equal. NaN logits are not supported.
+ *   workspace  at least idx_topk_workspace() bytes (NULL when that is 0).
+ *   Limits: 1 <= k <= 65536, rows >= 0, width >= 0.
+ */
+idx_status idx_topk(const float *logits, int64_t logits_row_stride, int32_t rows, int32_t width,
+                    const int32_t *row_start, const int32_t *row_end, int32_t k, int32_t *out,
+                    int64_t out_row_stride, void *workspace, size_t workspace_bytes, hipStream_t stream);
+size_t idx_topk_workspace(int32_t rows, int32_t width, int32_t k);
+
+/*
+ * idx_k_store - quantise key rows and write them into their cache slots.
+ * Page "vllm.models.deepseek_v41.amd.rocm", rocm_mxfp4_indexer_k_store (the
+ * quantise-and-write part; the RMSNorm and RoPE before it are not applied here).
+ *
+ *   k             [N, D] fp32 or bf16 (k_dtype), row i at k + i*k_row_stride
+ *                 (elements, >= D).
+ *   slot_mapping  [N] int64: key i goes to slot slot_mapping[i]; a negative slot
+ *                 skips the key (padding).
+ *   fp8:   scale = amax / 448 in fp32 (1.0 when the row is all zero); each value
+ *          becomes e4m3(k / scale) with an IEEE fp32 division, rounded to nearest
+ *          even and saturated at +-448.
+ *   MXFP4: per 32-value block, the e8m0 byte b is the smallest in [0, 254] with
+ *          amax <= 6 * 2^(b - 127); each value becomes e2m1(k * 2^(127 - b)),
+ *          rounded to nearest even (the e8m0 rule of _mxfp8_scale_bits on page
+ *          "vllm.v1.attention.ops.rocm_aiter_mla_sparse" with 6, the e2m1 maximum,
+ *          in place of 448).
+ *   Limits: D == 128, N >= 0.
+ */
+idx_status idx_k_store(const idx_paged_cache *cache, const void *k, int32_t k_dtype, int64_t k_row_stride,
+                       const int64_t *slot_mapping, int32_t N, hipStream_t stream);
+
+/*
+ * idx_q_quant - quantise query rows into the format the logits calls read.
+ * Page "vllm.models.deepseek_v41.amd.rocm", rocm_mxfp4_indexer_q_quant (the
+ * quantisation part: packed [T, H, D/2] plus one int32 of e8m0 bytes per head;
+ * RoPE and the weight scaling are not applied here).
+ *
+ *   q        [T, H, D] fp32 or bf16 (q_dtype), row t at q + t*q_row_stride
+ *            (elements, >= H*D), head h at + h*D.
+ *   fmt      IDX_KV_FP8_E4M3: q_out is [T, H, D] e4m3 (no scale: each value rounded
+ *            to nearest even, saturated at +-448); q_scale_out must be NULL.
+ *            IDX_KV_MXFP4_E2M1: q_out is [T, H, D/2] packed e2m1 and q_scale_out is
+ *            [T, H] int32 with the same block rule as idx_k_store.
+ *   Limits: D == 128, T, H >= 0.
+ */
+idx_status idx_q_quant(const void *q, int32_t q_dtype, int64_t q_row_stride, int32_t T, int32_t H, int32_t D,
+                       int32_t fmt, void *q_out, int32_t *q_scale_out, hipStream_t stream);
+
+/* Static text naming a status; never NULL. */
+const char *idx_status_str(idx_status s);
+/* IDX_ABI_VERSION of the built library. */
+int32_t idx_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IDX_H */

@@ -29,13 +29,18 @@ from . import cache, formats
 # ----------------------------------------------------------------------------------
 # logits
 # ----------------------------------------------------------------------------------
-def logits_from_values(q, k, w, starts, ends, k_scale=None, width=None) -> np.ndarray:
+def logits_from_values(q, k, w, starts, ends, k_scale=None, width=None, magnitude: bool = False) -> np.ndarray:
     """I[t, s] = sum_h w[t, h] * max(k_scale[s] * (q[t, h, :] . k[s, :]), 0) on
     [starts[t], ends[t]), -inf elsewhere.
 
     q is [M, H, D] and k is [N, D], both already dequantised to float64; k_scale is
     [N] or None (1.0). The result is [M, width] (width defaults to N); columns at or
     beyond N are -inf. Row ranges are clipped to [0, min(N, width)).
+
+    With ``magnitude`` the same walk returns instead
+    A[t, s] = sum_h |w[t, h]| * k_scale[s] * sum_d |q[t, h, d] * k[s, d]|, the scale of
+    the rounding error any summation-based evaluation of I[t, s] carries (the
+    tolerance of the parity tests is stated against it for ill-conditioned rows).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -47,6 +52,8 @@ def logits_from_values(q, k, w, starts, ends, k_scale=None, width=None) -> np.nd
     if M == 0 or N == 0 or width == 0:
         return out
     acc = np.zeros((M, N), dtype=np.float64)
+    if magnitude:
+        q, k, w = np.abs(q), np.abs(k), np.abs(w)
     for h in range(H):
         score = q[:, h, :] @ k.T  # [M, N]
         if k_scale is not None:
@@ -60,12 +67,12 @@ def logits_from_values(q, k, w, starts, ends, k_scale=None, width=None) -> np.nd
     return out
 
 
-def mqa_logits_fp8(q_codes, k_codes, k_scale, w, starts, ends) -> np.ndarray:
+def mqa_logits_fp8(q_codes, k_codes, k_scale, w, starts, ends, magnitude: bool = False) -> np.ndarray:
     """Contiguous fp8 chunk: q [M, H, D] e4m3, k [N, D] e4m3 + fp32 scale [N], w [M, H]
     fp32, rows valid on [starts, ends). Returns [M, N] float64."""
     return logits_from_values(
         formats.decode_e4m3(q_codes), formats.decode_e4m3(k_codes), w, starts, ends,
-        k_scale=np.asarray(k_scale, dtype=np.float32).reshape(-1))
+        k_scale=np.asarray(k_scale, dtype=np.float32).reshape(-1), magnitude=magnitude)
 
 
 # ----------------------------------------------------------------------------------
@@ -99,7 +106,7 @@ def _paged_keys(pool, fmt: str, P: int, D: int, block_table, b: int, L: int):
 
 
 def paged_logits(pool, fmt: str, P: int, block_table, context_lens, q, w, B: int, next_n: int,
-                 width: int, q_scale=None, per_row: bool = False) -> np.ndarray:
+                 width: int, q_scale=None, per_row: bool = False, magnitude: bool = False) -> np.ndarray:
     """Paged decode / MTP logits [B * next_n, width] (page
     ``vllm.v1.attention.ops.rocm_aiter_mla_sparse``, ``rocm_fp8_paged_mqa_logits``; page
     ``vllm.v1.attention.ops.rocm_paged_mxfp4_indexer``, ``rocm_mxfp4_sparse_attn_indexer``).
@@ -108,7 +115,8 @@ def paged_logits(pool, fmt: str, P: int, block_table, context_lens, q, w, B: int
     fmt "mxfp4": q [B, next_n, H, D/2] packed e2m1 with q_scale [B, next_n, H] int32
     (4 e8m0 bytes, byte j for block j), pool pages in the MXFP4 run layout.
     Row r = b * next_n + j is valid on [0, end_r) (``paged_row_ends``), clipped to the
-    width and to the keys the block table can address.
+    width and to the keys the block table can address. ``magnitude`` as in
+    ``logits_from_values``.
     """
     bt = np.asarray(block_table, dtype=np.int64)
     ends = paged_row_ends(context_lens, B, next_n, per_row)
@@ -128,7 +136,7 @@ def paged_logits(pool, fmt: str, P: int, block_table, context_lens, q, w, B: int
             continue
         kv, ks = _paged_keys(pool, fmt, P, D, bt, b, L)
         out[rows] = logits_from_values(qv[b], kv, w[rows], np.zeros(next_n, np.int64),
-                                       np.minimum(ends[rows], L), k_scale=ks, width=width)
+                                       np.minimum(ends[rows], L), k_scale=ks, width=width, magnitude=magnitude)
     return out
 
 

@@ -1,0 +1,68 @@
+"""Build libidx.so (the indexer's C ABI and its gfx950 HIP kernels) in-tree with hipcc.
+
+Every HIP source compiles for gfx950 only, with packed-fp32 instruction selection
+disabled (``-Xclang -target-feature -Xclang -packed-fp32-ops``; hipcc's host pass
+warns that it does not know the feature, which is harmless). Objects go to
+``_build/`` next to this file and the library to ``libidx.so`` beside it.
+
+    python -m sparse_attention_indexer_mxfp4_amd.build [-v]
+"""
+
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libidx.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+ARCH = "gfx950"
+COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
+          "-Wall", "-Wno-unused-function"]
+DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fno-gpu-flush-denormals-to-zero"]
+
+
+def sources() -> list[str]:
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+
+
+def _compile(src: str, extra: list[str]) -> tuple[str, str]:
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *COMMON, *extra]
+    if src.endswith(".hip"):
+        cmd += DEVICE + ["-x", "hip"]
+    cmd += ["-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return obj, r.stderr
+
+
+def build(verbose: bool = False, extra: list[str] | None = None, jobs: int = 8) -> str:
+    """Compile every source and link libidx.so; returns its path. Always rebuilds."""
+    os.makedirs(BUILD, exist_ok=True)
+    extra = list(extra or [])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        results = list(ex.map(lambda s: _compile(s, extra), sources()))
+    if verbose:
+        for obj, err in results:
+            noise = [ln for ln in err.splitlines() if "packed-fp32-ops" not in ln]
+            if noise:
+                print(obj, "\n".join(noise), file=sys.stderr)
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *[o for o, _ in results], "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,145 @@
+// The C ABI of libidx (declared in include/idx.h): argument checks, the device
+// check, and the launch of each call's kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+
+#include "../../include/idx.h"
+#include "launch.h"
+#include "validate.h"
+
+namespace {
+
+struct DeviceInfo {
+  bool known = false;
+  bool gfx950 = false;
+  int num_cus = 0;
+};
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+// Current device's properties, looked up once per device.
+idx_status current_device(int *num_cus) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return IDX_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceInfo &d = g_dev[dev];
+  if (!d.known) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return IDX_ERR_DEVICE;
+    d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.num_cus = prop.multiProcessorCount;
+    d.known = true;
+  }
+  if (!d.gfx950 || d.num_cus <= 0) return IDX_ERR_DEVICE;
+  *num_cus = d.num_cus;
+  return IDX_OK;
+}
+
+idx_status launched(hipError_t e) { return e == hipSuccess ? IDX_OK : IDX_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+size_t idx_page_bytes(int32_t fmt, int32_t page_size, int32_t head_dim) {
+  return idx::page_bytes(fmt, page_size, head_dim);
+}
+
+idx_status idx_mqa_logits(const uint8_t *q, int64_t q_row_stride, const uint8_t *k, int64_t k_row_stride,
+                          const float *k_scale, const float *w, int64_t w_row_stride,
+                          const int32_t *row_start, const int32_t *row_end, int32_t M, int32_t N, int32_t H,
+                          int32_t D, float *logits, int64_t logits_row_stride, hipStream_t stream) {
+  bool empty = false;
+  idx_status s = idx::check_mqa_logits(q, q_row_stride, k, k_row_stride, k_scale, w, w_row_stride, row_start,
+                                       row_end, M, N, H, D, logits, logits_row_stride, &empty);
+  if (s != IDX_OK || empty) return s;
+  int cus = 0;
+  if ((s = current_device(&cus)) != IDX_OK) return s;
+  idx::MqaArgs a{q, q_row_stride, k, k_row_stride, k_scale, w, w_row_stride, row_start, row_end,
+                 M, N, H, logits, logits_row_stride};
+  return launched(idx::launch_mqa_logits(a, cus, stream));
+}
+
+size_t idx_paged_mqa_logits_workspace(int32_t B, int32_t next_n, int32_t H, const idx_paged_cache *cache) {
+  return idx::paged_workspace_bytes(B, next_n, H, cache);
+}
+
+idx_status idx_paged_mqa_logits(const idx_paged_cache *cache, const void *q, const int32_t *q_scale,
+                                const float *w, const int32_t *context_lens, int32_t ctx_per_row,
+                                const int32_t *block_table, int64_t block_table_stride, int32_t max_blocks,
+                                int32_t B, int32_t next_n, int32_t H, float *logits, int64_t logits_row_stride,
+                                int32_t width, int32_t *row_end_out, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  bool empty = false;
+  idx_status s = idx::check_paged_mqa_logits(cache, q, q_scale, w, context_lens, block_table, block_table_stride,
+                                             max_blocks, B, next_n, H, logits, logits_row_stride, width,
+                                             workspace, workspace_bytes, &empty);
+  if (s != IDX_OK || empty) return s;
+  int cus = 0;
+  if ((s = current_device(&cus)) != IDX_OK) return s;
+  idx::PagedArgs a{static_cast<const uint8_t *>(cache->base), cache->page_stride_bytes, cache->page_size,
+                   cache->num_pages, cache->fmt, static_cast<const uint8_t *>(q), q_scale, w, context_lens,
+                   ctx_per_row != 0, block_table, block_table_stride, max_blocks, B, next_n, H, logits,
+                   logits_row_stride, width, row_end_out};
+  return launched(idx::launch_paged_logits(a, cus, stream));
+}
+
+size_t idx_topk_workspace(int32_t rows, int32_t width, int32_t k) { return idx::topk_workspace_bytes(rows, width, k); }
+
+idx_status idx_topk(const float *logits, int64_t logits_row_stride, int32_t rows, int32_t width,
+                    const int32_t *row_start, const int32_t *row_end, int32_t k, int32_t *out,
+                    int64_t out_row_stride, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  bool empty = false;
+  idx_status s = idx::check_topk(logits, logits_row_stride, rows, width, row_end, k, out, out_row_stride, workspace,
+                                 workspace_bytes, &empty);
+  if (s != IDX_OK || empty) return s;
+  int cus = 0;
+  if ((s = current_device(&cus)) != IDX_OK) return s;
+  idx::TopkArgs a{logits, logits_row_stride, rows, width, row_start, row_end, k, out, out_row_stride};
+  return launched(idx::launch_topk(a, cus, stream));
+}
+
+idx_status idx_k_store(const idx_paged_cache *cache, const void *k, int32_t k_dtype, int64_t k_row_stride,
+                       const int64_t *slot_mapping, int32_t N, hipStream_t stream) {
+  bool empty = false;
+  idx_status s = idx::check_k_store(cache, k, k_dtype, k_row_stride, slot_mapping, N, &empty);
+  if (s != IDX_OK || empty) return s;
+  int cus = 0;
+  if ((s = current_device(&cus)) != IDX_OK) return s;
+  idx::KStoreArgs a{static_cast<uint8_t *>(cache->base), cache->page_stride_bytes, cache->page_size,
+                    cache->num_pages, cache->fmt, k, k_dtype, k_row_stride, slot_mapping, N};
+  return launched(idx::launch_k_store(a, stream));
+}
+
+idx_status idx_q_quant(const void *q, int32_t q_dtype, int64_t q_row_stride, int32_t T, int32_t H, int32_t D,
+                       int32_t fmt, void *q_out, int32_t *q_scale_out, hipStream_t stream) {
+  bool empty = false;
+  idx_status s = idx::check_q_quant(q, q_dtype, q_row_stride, T, H, D, fmt, q_out, q_scale_out, &empty);
+  if (s != IDX_OK || empty) return s;
+  int cus = 0;
+  if ((s = current_device(&cus)) != IDX_OK) return s;
+  idx::QQuantArgs a{q, q_dtype, q_row_stride, T, H, fmt, static_cast<uint8_t *>(q_out), q_scale_out};
+  return launched(idx::launch_q_quant(a, stream));
+}
+
+const char *idx_status_str(idx_status s) {
+  switch (s) {
+    case IDX_OK: return "IDX_OK";
+    case IDX_ERR_NULL: return "IDX_ERR_NULL: a required pointer is NULL";
+    case IDX_ERR_SHAPE: return "IDX_ERR_SHAPE: a size is negative or outside the supported range";
+    case IDX_ERR_STRIDE: return "IDX_ERR_STRIDE: a stride or alignment requirement is not met";
+    case IDX_ERR_FORMAT: return "IDX_ERR_FORMAT: unknown format or dtype";
+    case IDX_ERR_WORKSPACE: return "IDX_ERR_WORKSPACE: workspace too small";
+    case IDX_ERR_LAUNCH: return "IDX_ERR_LAUNCH: kernel launch failed";
+    case IDX_ERR_DEVICE: return "IDX_ERR_DEVICE: no current gfx950 device";
+  }
+  return "unknown idx_status";
+}
+
+int32_t idx_abi_version(void) { return IDX_ABI_VERSION; }
+
+}  // extern "C"

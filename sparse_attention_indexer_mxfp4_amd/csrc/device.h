@@ -1,0 +1,119 @@
+// Device-side building blocks shared by the indexer kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace idx {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------------
+// Matrix cores: v_mfma_f32_16x16x128_f8f6f4 (gfx950), one 16x16 output tile with a
+// 128-deep contraction per instruction.
+//
+// Operand layout (checked on the device): lane L of A supplies row L % 16 and lane
+// L of B column L % 16, each with the 32 contraction elements of K-group L / 16
+// (32 bytes of e4m3, or 16 bytes of packed e2m1). C lands with rows
+// 4 * (L / 16) + j, j = 0..3, and column L % 16 in lane L. Which 32 of the 128
+// contraction indices a K-group holds does not matter as long as A and B agree, so
+// the kernels pick whatever byte order loads best. In the scaled fp4 form lane L's
+// scale byte multiplies its own 32-element block by 2^(byte - 127).
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ v4f mfma_fp8(const v8i &a, const v8i &b) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4f mfma_fp4(const v8i &a, const v8i &b, int scale_a, int scale_b) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 4, 0, scale_a, 0, scale_b);
+}
+
+// Sum of x over the four lanes L, L^16, L^32, L^48 (the four K-groups / C row
+// groups of an MFMA tile); every lane receives the total.
+__device__ __forceinline__ float sum_row_groups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ v4i load16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
+
+__device__ __forceinline__ v8i cat(const v4i &lo, const v4i &hi) {
+  v8i r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+__device__ __forceinline__ v8i zero8() {
+  v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
+  return r;
+}
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// ---------------------------------------------------------------------------------
+// Encoders of the K store and the query quantiser. Integer-exact, so they agree
+// bit for bit with any other correct implementation of the same rounding.
+// ---------------------------------------------------------------------------------
+
+// fp32 -> e4m3fn (OCP) byte: nearest finite value, ties to even, saturating at
+// +-448. NaN maps to the NaN code.
+__device__ __forceinline__ uint32_t enc_e4m3(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (!(a == a)) return sign | 0x7Fu;
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {
+    // below 2^-6 the e4m3 grid is m * 2^-9, m = 0..7 (m = 8 is the smallest
+    // normal, whose code is also 8); a * 512 is exact and rintf rounds to even
+    code = uint32_t(rintf(a * 512.0f));
+  } else {
+    int e = int((__float_as_uint(a) >> 23) & 0xFFu) - 127;               // -6..8
+    const float m = __uint_as_float((__float_as_uint(a) & 0x7FFFFFu) | 0x3F800000u);  // [1, 2)
+    uint32_t qm = uint32_t(rintf(m * 8.0f));                              // 8..16
+    if (qm == 16u) {
+      qm = 8u;
+      e += 1;
+    }
+    code = (uint32_t(e + 7) << 3) | (qm - 8u);
+  }
+  return sign | code;
+}
+
+// fp32 -> e2m1 nibble: nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even
+// code, saturating at +-6. The thresholds are the midpoints; a midpoint goes to
+// whichever neighbour has the even code.
+__device__ __forceinline__ uint32_t enc_e2m1(float x) {
+  const float a = fabsf(x);
+  const uint32_t c = uint32_t(a > 0.25f) + uint32_t(a >= 0.75f) + uint32_t(a > 1.25f) + uint32_t(a >= 1.75f) +
+                     uint32_t(a > 2.5f) + uint32_t(a >= 3.5f) + uint32_t(a > 5.0f);
+  return ((__float_as_uint(x) >> 28) & 0x8u) | c;
+}
+
+// Smallest e8m0 byte b in [0, 254] with amax <= 6 * 2^(b - 127), for finite
+// amax >= 0. Writing amax = f * 2^(E - 127) with f in [1, 2): the bound holds at
+// b = E - 2 when f <= 1.5 and needs b = E - 1 when f > 1.5; subnormal and zero
+// amax give a negative value, clamped to 0.
+__device__ __forceinline__ int e8m0_bits(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  const int E = int((u >> 23) & 0xFFu);
+  const int b = E - 2 + int((u & 0x7FFFFFu) > 0x400000u);
+  return b < 0 ? 0 : (b > 254 ? 254 : b);
+}
+
+// 2^(127 - b) for b in [0, 253] (normal fp32 throughout that range).
+__device__ __forceinline__ float e8m0_inv_scale(int b) {
+  const int ex = 254 - b;
+  return __uint_as_float(uint32_t(ex < 1 ? 1 : ex) << 23);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+}  // namespace idx

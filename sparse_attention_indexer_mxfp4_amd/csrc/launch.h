@@ -1,0 +1,86 @@
+// Kernel launchers behind the C ABI. Arguments reaching these have passed the host
+// checks of validate.h; each launcher only shapes the grid and enqueues.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace idx {
+
+struct MqaArgs {
+  const uint8_t *q;
+  int64_t q_row_stride;  // bytes
+  const uint8_t *k;
+  int64_t k_row_stride;  // bytes
+  const float *k_scale;
+  const float *w;
+  int64_t w_row_stride;  // elements
+  const int32_t *row_start;
+  const int32_t *row_end;
+  int32_t M, N, H;
+  float *logits;
+  int64_t logits_row_stride;  // elements
+};
+
+struct PagedArgs {
+  const uint8_t *base;
+  int64_t page_stride;  // bytes
+  int32_t page_size;
+  int32_t num_pages;
+  int32_t fmt;
+  const uint8_t *q;
+  const int32_t *q_scale;
+  const float *w;
+  const int32_t *context_lens;
+  int32_t ctx_per_row;
+  const int32_t *block_table;
+  int64_t block_table_stride;
+  int32_t max_blocks;
+  int32_t B, next_n, H;
+  float *logits;
+  int64_t logits_row_stride;
+  int32_t width;
+  int32_t *row_end_out;
+};
+
+struct TopkArgs {
+  const float *logits;
+  int64_t logits_row_stride;
+  int32_t rows, width;
+  const int32_t *row_start;
+  const int32_t *row_end;
+  int32_t k;
+  int32_t *out;
+  int64_t out_row_stride;
+};
+
+struct KStoreArgs {
+  uint8_t *base;
+  int64_t page_stride;
+  int32_t page_size;
+  int32_t num_pages;
+  int32_t fmt;
+  const void *k;
+  int32_t k_dtype;
+  int64_t k_row_stride;  // elements
+  const int64_t *slots;
+  int32_t N;
+};
+
+struct QQuantArgs {
+  const void *q;
+  int32_t q_dtype;
+  int64_t q_row_stride;  // elements
+  int32_t T, H;
+  int32_t fmt;
+  uint8_t *q_out;
+  int32_t *q_scale_out;
+};
+
+hipError_t launch_mqa_logits(const MqaArgs &a, int num_cus, hipStream_t stream);
+hipError_t launch_paged_logits(const PagedArgs &a, int num_cus, hipStream_t stream);
+hipError_t launch_topk(const TopkArgs &a, int num_cus, hipStream_t stream);
+hipError_t launch_k_store(const KStoreArgs &a, hipStream_t stream);
+hipError_t launch_q_quant(const QQuantArgs &a, hipStream_t stream);
+
+}  // namespace idx

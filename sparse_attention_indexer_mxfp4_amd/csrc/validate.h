@@ -1,0 +1,48 @@
+// Host-side argument checks of the indexer ABI. Plain C++ (no HIP), so the checks
+// can be exercised on a machine without a GPU. Each check returns IDX_OK, an
+// error, or IDX_OK with *empty set when the call has no work to launch.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/idx.h"
+
+namespace idx {
+
+constexpr int32_t kHeadDim = 128;
+constexpr int32_t kMaxHeads = 128;
+constexpr int32_t kMaxNextN = 4;
+constexpr int32_t kMaxBatch = 8192;
+constexpr int32_t kMaxTopK = 65536;
+
+size_t page_bytes(int32_t fmt, int32_t page_size, int32_t head_dim);
+
+idx_status check_cache(const idx_paged_cache *cache);
+
+idx_status check_mqa_logits(const void *q, int64_t q_row_stride, const void *k, int64_t k_row_stride,
+                            const void *k_scale, const void *w, int64_t w_row_stride, const void *row_start,
+                            const void *row_end, int32_t M, int32_t N, int32_t H, int32_t D, const void *logits,
+                            int64_t logits_row_stride, bool *empty);
+
+size_t paged_workspace_bytes(int32_t B, int32_t next_n, int32_t H, const idx_paged_cache *cache);
+
+idx_status check_paged_mqa_logits(const idx_paged_cache *cache, const void *q, const void *q_scale, const void *w,
+                                  const void *context_lens, const void *block_table, int64_t block_table_stride,
+                                  int32_t max_blocks, int32_t B, int32_t next_n, int32_t H, const void *logits,
+                                  int64_t logits_row_stride, int32_t width, const void *workspace,
+                                  size_t workspace_bytes, bool *empty);
+
+size_t topk_workspace_bytes(int32_t rows, int32_t width, int32_t k);
+
+idx_status check_topk(const void *logits, int64_t logits_row_stride, int32_t rows, int32_t width,
+                      const void *row_end, int32_t k, const void *out, int64_t out_row_stride,
+                      const void *workspace, size_t workspace_bytes, bool *empty);
+
+idx_status check_k_store(const idx_paged_cache *cache, const void *k, int32_t k_dtype, int64_t k_row_stride,
+                         const void *slot_mapping, int32_t N, bool *empty);
+
+idx_status check_q_quant(const void *q, int32_t q_dtype, int64_t q_row_stride, int32_t T, int32_t H, int32_t D,
+                         int32_t fmt, const void *q_out, const void *q_scale_out, bool *empty);
+
+}  // namespace idx

@@ -1,0 +1,163 @@
+"""Python binding of libidx: the C ABI's calls under the same names, taking PyTorch
+tensors for device memory and launching on PyTorch's current HIP stream.
+
+Argument marshalling only: every step runs in the library's HIP kernels. Shapes
+and dtypes are checked here only as far as needed to hand the right pointers and
+sizes over; the library checks everything it can see itself.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _abi
+from ._abi import IDX_IN_BF16, IDX_IN_F32, IDX_KV_FP8_E4M3, IDX_KV_MXFP4_E2M1, IdxError, PagedCache  # noqa: F401
+
+FP8 = IDX_KV_FP8_E4M3
+MXFP4 = IDX_KV_MXFP4_E2M1
+HEAD_DIM = 128
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t: torch.Tensor, dtype, name: str, device=None) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name}: expected a device tensor")
+
+
+def _contig(t: torch.Tensor, name: str) -> None:
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def page_bytes(fmt: int, page_size: int, head_dim: int = HEAD_DIM) -> int:
+    return int(_abi.lib().idx_page_bytes(fmt, page_size, head_dim))
+
+
+def paged_cache(pool: torch.Tensor, fmt: int, page_size: int, head_dim: int = HEAD_DIM) -> PagedCache:
+    """Descriptor of a pool tensor [num_pages, page_stride_bytes] uint8 (page rows may be
+    padded beyond the page size)."""
+    _need(pool, torch.uint8, "pool")
+    if pool.dim() != 2 or pool.stride(1) != 1:
+        raise ValueError("pool must be [num_pages, page_stride_bytes] with unit inner stride")
+    return PagedCache(fmt=fmt, page_size=page_size, num_pages=pool.shape[0], head_dim=head_dim,
+                      page_stride_bytes=pool.stride(0), base=pool.data_ptr())
+
+
+def idx_mqa_logits(q: torch.Tensor, k: torch.Tensor, k_scale: torch.Tensor, w: torch.Tensor,
+                   row_start: torch.Tensor, row_end: torch.Tensor, logits: torch.Tensor | None = None) -> torch.Tensor:
+    """Contiguous fp8 logits. q [M, H, 128] uint8 (e4m3 bytes), k [N, 128] uint8, k_scale [N]
+    f32, w [M, H] f32, row_start/row_end [M] int32 -> logits [M, N] f32."""
+    _need(q, torch.uint8, "q"); _need(k, torch.uint8, "k"); _need(k_scale, torch.float32, "k_scale")
+    _need(w, torch.float32, "w"); _need(row_start, torch.int32, "row_start"); _need(row_end, torch.int32, "row_end")
+    M, H, D = q.shape
+    N = k.shape[0]
+    if q.stride(2) != 1 or q.stride(1) != D or k.stride(1) != 1 or w.stride(1) != 1:
+        raise ValueError("q heads, k rows and w rows must be dense")
+    _contig(k_scale, "k_scale"); _contig(row_start, "row_start"); _contig(row_end, "row_end")
+    if logits is None:
+        logits = torch.empty((M, (N + 3) // 4 * 4), dtype=torch.float32, device=q.device)[:, :N]
+    _need(logits, torch.float32, "logits")
+    _abi.check(_abi.lib().idx_mqa_logits(
+        _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(k_scale), _ptr(w), w.stride(0), _ptr(row_start),
+        _ptr(row_end), M, N, H, D, _ptr(logits), logits.stride(0), _stream()))
+    return logits
+
+
+def idx_paged_mqa_logits(pool: torch.Tensor, fmt: int, page_size: int, q: torch.Tensor, q_scale: torch.Tensor | None,
+                         w: torch.Tensor, context_lens: torch.Tensor, block_table: torch.Tensor, width: int,
+                         ctx_per_row: bool = False, logits: torch.Tensor | None = None,
+                         row_end_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Paged decode / MTP logits. q [B, next_n, H, 128] (fp8) or [B, next_n, H, 64] (MXFP4) uint8,
+    q_scale [B, next_n, H] int32 (MXFP4) or None, w [B*next_n, H] f32, context_lens [B] (or
+    [B*next_n] with ctx_per_row) int32, block_table [B, max_blocks] int32.
+    Returns (logits [B*next_n, width] f32, row_end [B*next_n] int32)."""
+    cache = paged_cache(pool, fmt, page_size)
+    _need(q, torch.uint8, "q"); _need(w, torch.float32, "w"); _need(context_lens, torch.int32, "context_lens")
+    _need(block_table, torch.int32, "block_table")
+    _contig(q, "q"); _contig(w, "w"); _contig(context_lens, "context_lens")
+    if q_scale is not None:
+        _need(q_scale, torch.int32, "q_scale"); _contig(q_scale, "q_scale")
+    if block_table.stride(1) != 1:
+        raise ValueError("block_table rows must be dense")
+    B, next_n, H = q.shape[:3]
+    rows = B * next_n
+    if logits is None:
+        logits = torch.empty((rows, (width + 3) // 4 * 4), dtype=torch.float32, device=q.device)[:, :width]
+    if row_end_out is None:
+        row_end_out = torch.empty(rows, dtype=torch.int32, device=q.device)
+    lib = _abi.lib()
+    need = lib.idx_paged_mqa_logits_workspace(B, next_n, H, ctypes.byref(cache))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _abi.check(lib.idx_paged_mqa_logits(
+        ctypes.byref(cache), _ptr(q), _ptr(q_scale), _ptr(w), _ptr(context_lens), int(ctx_per_row),
+        _ptr(block_table), block_table.stride(0), block_table.shape[1], B, next_n, H, _ptr(logits),
+        logits.stride(0), width, _ptr(row_end_out), _ptr(workspace), ws_bytes, _stream()))
+    return logits, row_end_out
+
+
+def idx_topk(logits: torch.Tensor, row_start: torch.Tensor | None, row_end: torch.Tensor, k: int,
+             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Per-row top-k over [row_start, row_end) -> [rows, k] int32 (column - start, ascending
+    column order, -1 padded)."""
+    _need(logits, torch.float32, "logits"); _need(row_end, torch.int32, "row_end")
+    _contig(row_end, "row_end")
+    if row_start is not None:
+        _need(row_start, torch.int32, "row_start"); _contig(row_start, "row_start")
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be dense")
+    rows, width = logits.shape
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=logits.device)
+    lib = _abi.lib()
+    need = lib.idx_topk_workspace(rows, width, k)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _abi.check(lib.idx_topk(_ptr(logits), logits.stride(0), rows, width, _ptr(row_start), _ptr(row_end), k,
+                            _ptr(out), out.stride(0), _ptr(workspace), ws_bytes, _stream()))
+    return out
+
+
+def idx_k_store(pool: torch.Tensor, fmt: int, page_size: int, k: torch.Tensor, slot_mapping: torch.Tensor) -> None:
+    """Quantise key rows k [N, 128] (f32 or bf16) into their slots of the pool."""
+    cache = paged_cache(pool, fmt, page_size)
+    if k.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("k must be float32 or bfloat16")
+    _need(slot_mapping, torch.int64, "slot_mapping"); _contig(slot_mapping, "slot_mapping")
+    if k.stride(1) != 1:
+        raise ValueError("k rows must be dense")
+    dt = IDX_IN_F32 if k.dtype == torch.float32 else IDX_IN_BF16
+    _abi.check(_abi.lib().idx_k_store(ctypes.byref(cache), _ptr(k), dt, k.stride(0), _ptr(slot_mapping),
+                                      k.shape[0], _stream()))
+
+
+def idx_q_quant(q: torch.Tensor, fmt: int):
+    """Quantise query rows q [T, H, 128] (f32 or bf16). fp8 -> ([T, H, 128] uint8, None);
+    MXFP4 -> ([T, H, 64] uint8, [T, H] int32)."""
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("q must be float32 or bfloat16")
+    T, H, D = q.shape
+    if q.stride(2) != 1 or q.stride(1) != D:
+        raise ValueError("q heads must be dense")
+    dt = IDX_IN_F32 if q.dtype == torch.float32 else IDX_IN_BF16
+    if fmt == FP8:
+        out = torch.empty((T, H, D), dtype=torch.uint8, device=q.device)
+        scale = None
+    else:
+        out = torch.empty((T, H, D // 2), dtype=torch.uint8, device=q.device)
+        scale = torch.empty((T, H), dtype=torch.int32, device=q.device)
+    _abi.check(_abi.lib().idx_q_quant(_ptr(q), dt, q.stride(0), T, H, D, fmt, _ptr(out), _ptr(scale), _stream()))
+    return out, scale

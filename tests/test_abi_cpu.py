@@ -1,0 +1,173 @@
+"""The C ABI without a GPU: the library loads, exports every function include/idx.h
+declares, and its host-side checks reject bad arguments before any launch (each
+call here fails a check, so nothing reaches the device)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from sparse_attention_indexer_mxfp4_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "idx.h")
+
+OK, NULL, SHAPE, STRIDE, FORMAT, WORKSPACE, LAUNCH, DEVICE = range(8)
+P = 0x10000  # an aligned, never-dereferenced stand-in address
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _abi.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(idx_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared()
+    assert "idx_mqa_logits" in names and "idx_topk" in names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert sorted(names) == sorted(_abi.EXPORTS)
+
+
+def test_version_and_status_text(lib):
+    assert lib.idx_abi_version() == 1
+    for s in range(8):
+        assert lib.idx_status_str(s).decode().startswith(_abi.STATUS_NAMES[s])
+    assert lib.idx_status_str(99) == b"unknown idx_status"
+
+
+def test_page_bytes(lib):
+    assert lib.idx_page_bytes(0, 64, 128) == 64 * 132
+    assert lib.idx_page_bytes(1, 64, 128) == 64 * 68
+    assert lib.idx_page_bytes(7, 64, 128) == 0
+
+
+def _mqa(lib, **kw):
+    a = dict(q=P, qs=64 * 128, k=P, ks=128, ksc=P, w=P, ws=64, rs=P, re=P, M=8, N=100, H=64, D=128, out=P, os=100)
+    a.update(kw)
+    return lib.idx_mqa_logits(a["q"], a["qs"], a["k"], a["ks"], a["ksc"], a["w"], a["ws"], a["rs"], a["re"], a["M"],
+                              a["N"], a["H"], a["D"], a["out"], a["os"], None)
+
+
+def test_mqa_logits_checks(lib):
+    assert _mqa(lib, D=64) == SHAPE
+    assert _mqa(lib, H=0) == SHAPE
+    assert _mqa(lib, H=129) == SHAPE
+    assert _mqa(lib, M=-1) == SHAPE
+    assert _mqa(lib, M=0) == OK  # empty: nothing launched
+    assert _mqa(lib, N=0, q=None) == OK
+    assert _mqa(lib, q=None) == NULL
+    assert _mqa(lib, ksc=None) == NULL
+    assert _mqa(lib, out=None) == NULL
+    assert _mqa(lib, qs=64 * 128 - 16) == STRIDE
+    assert _mqa(lib, q=P + 8) == STRIDE
+    assert _mqa(lib, ks=100) == STRIDE
+    assert _mqa(lib, os=99) == STRIDE
+    assert _mqa(lib, os=102) == STRIDE
+    assert _mqa(lib, out=P + 4) == STRIDE
+    assert _mqa(lib, ws=10) == STRIDE
+
+
+def _cache(fmt=0, ps=64, npg=10, hd=128, stride=None, base=P):
+    pb = ps * (hd + 4) if fmt == 0 else ps * (hd // 2 + hd // 32)
+    return _abi.PagedCache(fmt=fmt, page_size=ps, num_pages=npg, head_dim=hd,
+                           page_stride_bytes=pb if stride is None else stride, base=base)
+
+
+def _paged(lib, cache=None, **kw):
+    a = dict(q=P, qsc=None, w=P, ctx=P, per_row=0, bt=P, bts=8, mb=8, B=4, nn=1, H=64, out=P, os=512, width=512,
+             ends=None, ws=None, wsb=0)
+    a.update(kw)
+    c = _cache() if cache is None else cache
+    return lib.idx_paged_mqa_logits(ctypes.byref(c), a["q"], a["qsc"], a["w"], a["ctx"], a["per_row"], a["bt"],
+                                    a["bts"], a["mb"], a["B"], a["nn"], a["H"], a["out"], a["os"], a["width"],
+                                    a["ends"], a["ws"], a["wsb"], None)
+
+
+def test_paged_checks(lib):
+    assert lib.idx_paged_mqa_logits(None, P, None, P, P, 0, P, 8, 8, 4, 1, 64, P, 512, 512, None, None, 0,
+                                    None) == NULL
+    assert _paged(lib, cache=_cache(fmt=3)) == FORMAT
+    assert _paged(lib, cache=_cache(hd=64)) == SHAPE
+    assert _paged(lib, cache=_cache(ps=40)) == SHAPE
+    assert _paged(lib, cache=_cache(ps=2048)) == SHAPE
+    assert _paged(lib, cache=_cache(npg=0)) == SHAPE
+    assert _paged(lib, cache=_cache(stride=64 * 132 - 16)) == STRIDE
+    assert _paged(lib, cache=_cache(stride=64 * 132 + 4)) == STRIDE
+    assert _paged(lib, cache=_cache(base=None)) == NULL
+    assert _paged(lib, cache=_cache(base=P + 4)) == STRIDE
+    assert _paged(lib, nn=0) == SHAPE
+    assert _paged(lib, nn=5) == SHAPE
+    assert _paged(lib, B=8193) == SHAPE
+    assert _paged(lib, H=200) == SHAPE
+    assert _paged(lib, width=-1) == SHAPE
+    assert _paged(lib, B=8192, width=2 ** 31 - 1) == SHAPE  # chunk offsets would overflow int32
+    assert _paged(lib, B=0, q=None) == OK
+    assert _paged(lib, q=None) == NULL
+    assert _paged(lib, ctx=None) == NULL
+    assert _paged(lib, bt=None) == NULL
+    assert _paged(lib, out=None) == NULL
+    assert _paged(lib, qsc=P) == FORMAT  # fp8 carries no query scale
+    assert _paged(lib, cache=_cache(fmt=1)) == NULL  # MXFP4 needs one
+    assert _paged(lib, bts=7) == STRIDE
+    assert _paged(lib, os=510) == STRIDE
+    assert _paged(lib, out=P + 8) == STRIDE
+    assert _paged(lib, q=P + 1) == STRIDE
+
+
+def test_workspace_queries(lib):
+    c = _cache()
+    assert lib.idx_paged_mqa_logits_workspace(4, 1, 64, ctypes.byref(c)) == 0
+    assert lib.idx_topk_workspace(4, 1000, 16) == 0
+
+
+def _topk(lib, **kw):
+    a = dict(L=P, ls=1000, rows=4, width=1000, rs=None, re=P, k=16, out=P, os=16, ws=None, wsb=0)
+    a.update(kw)
+    return lib.idx_topk(a["L"], a["ls"], a["rows"], a["width"], a["rs"], a["re"], a["k"], a["out"], a["os"], a["ws"],
+                        a["wsb"], None)
+
+
+def test_topk_checks(lib):
+    assert _topk(lib, k=0) == SHAPE
+    assert _topk(lib, k=65537) == SHAPE
+    assert _topk(lib, rows=-1) == SHAPE
+    assert _topk(lib, rows=0, L=None, re=None, out=None) == OK
+    assert _topk(lib, re=None) == NULL
+    assert _topk(lib, out=None) == NULL
+    assert _topk(lib, L=None) == NULL
+    assert _topk(lib, ls=999) == STRIDE
+    assert _topk(lib, os=15) == STRIDE
+    assert _topk(lib, out=P + 2) == STRIDE
+
+
+def test_k_store_and_q_quant_checks(lib):
+    c = _cache()
+    assert lib.idx_k_store(ctypes.byref(c), P, 2, 128, P, 10, None) == FORMAT
+    assert lib.idx_k_store(ctypes.byref(c), P, 0, 128, P, -1, None) == SHAPE
+    assert lib.idx_k_store(ctypes.byref(c), None, 0, 128, None, 0, None) == OK
+    assert lib.idx_k_store(ctypes.byref(c), None, 0, 128, P, 10, None) == NULL
+    assert lib.idx_k_store(ctypes.byref(c), P, 0, 127, P, 10, None) == STRIDE
+    assert lib.idx_k_store(ctypes.byref(c), P + 2, 0, 128, P, 10, None) == STRIDE
+    assert lib.idx_k_store(ctypes.byref(c), P, 0, 128, P + 4, 10, None) == STRIDE
+    assert lib.idx_q_quant(P, 0, 128, 4, 1, 128, 5, P, None, None) == FORMAT
+    assert lib.idx_q_quant(P, 3, 128, 4, 1, 128, 0, P, None, None) == FORMAT
+    assert lib.idx_q_quant(P, 0, 128, 4, 1, 64, 0, P, None, None) == SHAPE
+    assert lib.idx_q_quant(None, 0, 128, 0, 1, 128, 0, None, None, None) == OK
+    assert lib.idx_q_quant(P, 0, 128, 4, 1, 128, 1, P, None, None) == NULL
+    assert lib.idx_q_quant(P, 0, 128, 4, 1, 128, 0, P, P, None) == FORMAT
+    assert lib.idx_q_quant(P, 0, 100, 4, 1, 128, 0, P, None, None) == STRIDE
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path; a GPU is visible")
+def test_valid_call_without_device_reports_device_error(lib):
+    # arguments pass every host check, so the call reaches the device query, which
+    # fails here because this machine has no GPU; nothing is launched
+    assert _topk(lib) == DEVICE
