@@ -81,7 +81,10 @@ idx_status idx_paged_mqa_logits(const idx_paged_cache *cache, const void *q, con
   if (s != IDX_OK || empty) return s;
   int cus = 0;
   if ((s = current_device(&cus)) != IDX_OK) return s;
-  idx::PagedArgs a{static_cast<const uint8_t *>(cache->base), cache->page_stride_bytes, cache->page_size,
+  int shift = -1;
+  for (int sh = 4; sh <= 10; ++sh)
+    if (cache->page_size == (1 << sh)) shift = sh;
+  idx::PagedArgs a{static_cast<const uint8_t *>(cache->base), cache->page_stride_bytes, cache->page_size, shift,
                    cache->num_pages, cache->fmt, static_cast<const uint8_t *>(q), q_scale, w, context_lens,
                    ctx_per_row != 0, block_table, block_table_stride, max_blocks, B, next_n, H, logits,
                    logits_row_stride, width, row_end_out};

@@ -40,7 +40,31 @@ __device__ __forceinline__ float sum_row_groups(float x) {
   return x;
 }
 
+// Four partial sums per lane, p[kg] for the 16 keys kg*16 + L%16, reduced over the
+// four lane groups and delivered transposed: lane L gets the total of
+// p[L/16] over lanes L%16, L%16+16, L%16+32, L%16+48, i.e. the full sum for key L
+// of a 64-key chunk. v_permlane32_swap exchanges the upper 32 lanes of its first
+// operand with the lower 32 of its second, v_permlane16_swap the odd 16-lane rows of
+// the first with the even rows of the second; three swaps and three adds replace
+// eight cross-lane shuffles.
+__device__ __forceinline__ float transpose_reduce4(const float (&p)[4]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
+  const float s02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const float s13 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 __device__ __forceinline__ v4i load16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
+
+// max(x, 0) as one integer max on the bit pattern: negative floats are negative
+// integers, so they (and -0.0) become +0.0 and non-negative floats pass unchanged.
+// fmaxf would first canonicalise its input (a second VALU op) under IEEE mode.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// A value the compiler may treat as wavefront-uniform (kept in a scalar register).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 __device__ __forceinline__ v8i cat(const v4i &lo, const v4i &hi) {
   v8i r;

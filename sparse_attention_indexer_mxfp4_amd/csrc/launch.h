@@ -26,6 +26,7 @@ struct PagedArgs {
   const uint8_t *base;
   int64_t page_stride;  // bytes
   int32_t page_size;
+  int32_t page_shift;  // log2(page_size) when it is a power of two, else -1
   int32_t num_pages;
   int32_t fmt;
   const uint8_t *q;

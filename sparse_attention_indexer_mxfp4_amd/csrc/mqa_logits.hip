@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
   __shared__ int s_range[2];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4;
   const int n = lane & 15;
@@ -130,9 +130,7 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
     if (tid < kChunk) ss[tid] = (c + tid < a.N) ? a.k_scale[c + tid] : 0.f;
     __syncthreads();
 
-    float res[kRowsPerWave];
-#pragma unroll
-    for (int rr = 0; rr < kRowsPerWave; ++rr) res[rr] = 0.f;
+    float part[kRowsPerWave][4];
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg) {
       const uint8_t *kp = sk + (kg * 16 + n) * kKeyStride + g * 16;
@@ -144,12 +142,14 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
         for (int ht = 0; ht < HT; ++ht) {
           const v4f s = mfma_fp8(qa[rr][ht], kb);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc = fmaf(wv[rr][ht][j], fmaxf(s[j], 0.f), acc);
+          for (int j = 0; j < 4; ++j) acc = fmaf(wv[rr][ht][j], relu(s[j]), acc);
         }
-        acc = sum_row_groups(acc);
-        if (g == kg) res[rr] = acc;
+        part[rr][kg] = acc;
       }
     }
+    float res[kRowsPerWave];
+#pragma unroll
+    for (int rr = 0; rr < kRowsPerWave; ++rr) res[rr] = transpose_reduce4(part[rr]);
     const int col = c + lane;
     const float sc = ss[lane];
 #pragma unroll

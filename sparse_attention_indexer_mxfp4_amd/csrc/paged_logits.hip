@@ -6,23 +6,35 @@
 // rocm_fp8_paged_mqa_logits; page "vllm.v1.attention.ops.rocm_paged_mxfp4_indexer",
 // rocm_mxfp4_sparse_attn_indexer. Every column of [0, width) is written.
 //
-// The step is HBM-bound: each key's bytes are read once for all next_n rows of its
-// sequence and all heads. Work unit = one 64-key chunk of one sequence. Every
-// workgroup first computes the prefix sum of chunks per sequence in LDS (from
-// context_lens, on the device, so the grid never depends on lengths), then each
-// wave takes an equal contiguous share of the concatenated chunk list, whatever
-// the mix of lengths. Waves of workgroups on the same XCD get neighbouring shares,
-// so a sequence's queries and block-table row stay in one L2. A wave holds its
-// sequence's queries as MFMA A operands (16 heads x 128 channels per tile) and
-// reads each 16-key group of a page straight into B operands:
+// The step streams the K cache once (HBM-bound). The work unit is a 64-key chunk of
+// one sequence; all next_n rows of the sequence are scored from the same bytes.
+// Every workgroup of a persistent grid first builds, in LDS, the prefix sum of chunk
+// counts over the sequences (from context_lens on the device, so the grid never
+// depends on lengths), and each wave takes an equal contiguous share of the
+// concatenated chunk list, whatever the mix of lengths (at least a few chunks, so a
+// wave's query reloads stay small next to its K bytes). Waves of one XCD get
+// neighbouring shares, so a sequence's queries stay in one L2. A wave
+//   - fetches the block-table entries of its next 16 chunks with one vector load
+//     (lane l: chunk l/4, 16-key group l%4) and reads them back with readlane;
+//   - keeps two chunks in registers: the loads of chunk i+1 are in flight while
+//     chunk i is scored;
+//   - holds its sequence's queries as MFMA A operands (16 heads x 128 channels per
+//     tile), reloading them when its share crosses into the next sequence.
+// K bytes go straight into MFMA B operands:
 //   fp8   lane L loads key L%16's bytes [16g, 16g+16) and [64+16g, 64+16g+16),
 //         g = L/16, from the block-flat page (the query uses the same byte order);
 //   MXFP4 lane L loads 16 bytes at run base + 16L - the run stores [chunk, key,
 //         byte], so one wavefront load covers the run's kilobyte exactly and lands
 //         in the scaled MFMA's operand order - plus the e8m0 byte at
 //         scale base + 64 * run + L, which is that lane's own block scale.
-// After the compute share, every wave writes an equal share of the -inf tail
-// (columns past the last chunk of each row's sequence) with 16-byte stores.
+// The epilogue sums ReLU(score) * w over the 16 heads of each lane (4 per tile), then
+// over the four lane groups with a transposed permlane reduction that leaves key L of
+// the chunk in lane L, scales by the key's fp32 scale (fp8; k_scale > 0 so it factors
+// out of the ReLU) and stores one 256-byte segment per row and chunk. Every wave also
+// writes an equal share of the -inf tail (columns past the last chunk of each row's
+// sequence) with 16-byte stores, issued before its K loads.
+#include <mutex>
+
 #include "device.h"
 #include "launch.h"
 
@@ -31,25 +43,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChunk = 64;
-
-struct SeqRows {
-  int end[4];
-  int len;
-};
-
-template <int NR>
-__device__ __forceinline__ SeqRows seq_rows(const PagedArgs &a, int b, int cap) {
-  SeqRows s;
-  s.len = 0;
-#pragma unroll
-  for (int j = 0; j < NR; ++j) {
-    int e = a.ctx_per_row ? a.context_lens[b * NR + j] : a.context_lens[b] - NR + j + 1;
-    e = min(max(e, 0), cap);
-    s.end[j] = e;
-    s.len = max(s.len, e);
-  }
-  return s;
-}
+constexpr int kMinChunksPerWave = 4;
 
 // Exclusive prefix sum of per-thread values over the workgroup; returns the
 // thread's offset and stores the total in *total.
@@ -74,198 +68,332 @@ __device__ int block_exclusive_scan(int v, int *scratch, int *total) {
   return before + x - v;
 }
 
+// largest b in [0, B) with pref[b] <= u (pref[B] > u)
+__device__ __forceinline__ int find_seq(const int *pref, int B, int u) {
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pref[mid] <= u) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+template <int NR>
+__device__ __forceinline__ void row_ends(const PagedArgs &a, int b, int cap, int (&end)[NR]) {
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const int e = a.ctx_per_row ? a.context_lens[b * NR + j] : a.context_lens[b] - NR + j + 1;
+    end[j] = min(max(e, 0), cap);
+  }
+}
+
+template <int FMT>
+struct Chunk {
+  v8i kb[4];
+  int ksb[4];
+  float ksc;
+};
+
 template <int FMT, int HT, int NR>
 __global__ __launch_bounds__(kThreads) void paged_logits_kernel(PagedArgs a) {
-  extern __shared__ int s_pref[];  // B + 1 chunk offsets
+  extern __shared__ int s_lds[];  // pref[B + 1], len[B]
   __shared__ int s_scan[kThreads / 64];
+  int *s_pref = s_lds;
+  int *s_len = s_lds + a.B + 1;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4;
   const int n = lane & 15;
   const int P = a.page_size;
   const int cap = int(min(int64_t(a.width), int64_t(a.max_blocks) * P));
 
-  // ---- chunk counts per sequence and their prefix sum (LDS) -------------------
+  // ---- chunks per sequence, their prefix sum, sequence lengths (LDS) -------------
   const int per = (a.B + kThreads - 1) / kThreads;
   const int b_lo = min(a.B, tid * per), b_hi = min(a.B, b_lo + per);
   int mine = 0;
-  for (int b = b_lo; b < b_hi; ++b) mine += (seq_rows<NR>(a, b, cap).len + kChunk - 1) / kChunk;
+  for (int b = b_lo; b < b_hi; ++b) {
+    int end[NR];
+    row_ends<NR>(a, b, cap, end);
+    int len = 0;
+#pragma unroll
+    for (int j = 0; j < NR; ++j) len = max(len, end[j]);
+    s_len[b] = len;
+    mine += (len + kChunk - 1) / kChunk;
+  }
   int total = 0;
   int run = block_exclusive_scan(mine, s_scan, &total);
   for (int b = b_lo; b < b_hi; ++b) {
     s_pref[b] = run;
-    run += (seq_rows<NR>(a, b, cap).len + kChunk - 1) / kChunk;
+    run += (s_len[b] + kChunk - 1) / kChunk;
   }
   if (tid == 0) s_pref[a.B] = total;
   if (blockIdx.x == 0 && a.row_end_out) {
-    for (int r = tid; r < a.B * NR; r += kThreads) a.row_end_out[r] = seq_rows<NR>(a, r / NR, cap).end[r % NR];
+    for (int r = tid; r < a.B * NR; r += kThreads) {
+      int end[NR];
+      row_ends<NR>(a, r / NR, cap, end);
+      int e = end[0];
+#pragma unroll
+      for (int j = 1; j < NR; ++j)
+        if (r % NR == j) e = end[j];
+      a.row_end_out[r] = e;
+    }
   }
   __syncthreads();
 
-  // ---- this wave's share of the chunk list -------------------------------------
-  const int nwg = gridDim.x;  // a multiple of 8 (one slice per XCD)
+  // ---- this wave's share of the chunk list ---------------------------------------
+  // Shares go to waves spread evenly over the whole grid (and so over every XCD)
+  // when there are fewer shares than waves; neighbouring shares land on waves of
+  // the same XCD.
+  const int nwg = gridDim.x;  // a multiple of 8: one slice of workgroups per XCD
   const int logical = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
-  const int64_t V = int64_t(nwg) * (kThreads / 64);
-  const int64_t v = int64_t(logical) * (kThreads / 64) + wave;
-  const int64_t U = total;
-  const int u0 = int(U * v / V), u1 = int(U * (v + 1) / V);
+  const int V = nwg * (kThreads / 64);
+  const int v = logical * (kThreads / 64) + wave;
+  const int U = total;
+  const int used = min(V, max(1, (U + kMinChunksPerWave - 1) / kMinChunksPerWave));
+  const int k = int(int64_t(v) * used / V);
+  const bool owner = v == 0 || int(int64_t(v - 1) * used / V) != k;
+  const int u0 = owner ? int(int64_t(U) * k / used) : U;
+  const int u1 = owner ? int(int64_t(U) * (k + 1) / used) : U;
+  const float ninf = neg_inf();
 
-  int b = -1, b_next = 0;
-  SeqRows rows;
-  v8i qa[NR][HT];
-  float wv[NR][HT][4];
-  int qs[NR][HT];
-  const int32_t *bt_row = a.block_table;
-
-  for (int u = u0; u < u1; ++u) {
-    if (u >= b_next) {
-      // largest b with s_pref[b] <= u; s_pref[B] = total > u bounds it to [0, B)
-      int lo = 0, hi = a.B;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_pref[mid] <= u) lo = mid; else hi = mid;
-      }
-      b = lo;
-      b_next = s_pref[b + 1];
-      rows = seq_rows<NR>(a, b, cap);
-      bt_row = a.block_table + int64_t(b) * a.block_table_stride;
-#pragma unroll
-      for (int j = 0; j < NR; ++j) {
-        const int64_t r = int64_t(b) * NR + j;
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-          const int h = ht * 16 + n;
-          if (h < a.H) {
-            if (FMT == 0) {
-              const uint8_t *p = a.q + (r * a.H + h) * 128 + g * 16;
-              qa[j][ht] = cat(load16(p), load16(p + 64));
-              qs[j][ht] = 0;
-            } else {
-              const uint8_t *p = a.q + (r * a.H + h) * 64 + g * 16;
-              const v4i z = {0, 0, 0, 0};
-              qa[j][ht] = cat(load16(p), z);
-              qs[j][ht] = (a.q_scale[r * a.H + h] >> (8 * g)) & 0xFF;
-            }
-          } else {
-            qa[j][ht] = zero8();
-            qs[j][ht] = 127;
-          }
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int hh = ht * 16 + 4 * g + jj;
-            wv[j][ht][jj] = hh < a.H ? a.w[r * a.H + hh] : 0.f;
-          }
+  // ---- -inf past each sequence's last chunk (issued first: the stores drain while
+  // the K loads below are in flight) ---------------------------------------------------
+  {
+    const int NU = (a.width + 255) / 256;
+    const int64_t R = int64_t(a.B) * NR;
+    for (int64_t f = v; f < R * NU; f += V) {
+      const int64_t r = f / NU;
+      const int col = int(f % NU) * 256 + lane * 4;
+      const int bb = int(r / NR);
+      const int tail = (s_pref[bb + 1] - s_pref[bb]) * kChunk;
+      if (col >= tail && col < a.width) {
+        float *p = a.logits + r * a.logits_row_stride + col;
+        if (col + 4 <= a.width) {
+          *reinterpret_cast<v4f *>(p) = v4f{ninf, ninf, ninf, ninf};
+        } else {
+          for (int i = 0; col + i < a.width; ++i) p[i] = ninf;
         }
       }
     }
+  }
 
-    const int key0 = (u - s_pref[b]) * kChunk;
-    v8i kb[4];
-    int ksb[4];
-    float ksc = 0.f;
-    const uint8_t *scale_ptr = nullptr;
+  // block-table entries of chunks [base, base + 16): lane l holds chunk base + l/4,
+  // 16-key group l%4 (0 past the wave's share or the sequence's end)
+  auto load_pages = [&](int base) -> int {
+    const int u = base + (lane >> 2);
+    int pg = 0;
+    if (u < u1) {
+      const int bb = find_seq(s_pref, a.B, u);
+      const int s = (u - s_pref[bb]) * kChunk + (lane & 3) * 16;
+      if (s < s_len[bb]) {
+        const int pi = a.page_shift >= 0 ? s >> a.page_shift : s / P;
+        pg = min(max(a.block_table[int64_t(bb) * a.block_table_stride + pi], 0), a.num_pages - 1);
+      }
+    }
+    return pg;
+  };
+
+  // issue the loads of chunk `c` (index within sequence `b`) whose pages sit in lanes
+  // 4*slot .. 4*slot+3 of `pg`
+  auto issue = [&](Chunk<FMT> &ch, int pg, int slot, int b, int c) {
+    const int key0 = c * kChunk;
+    const int len = s_len[b];
+    ch.ksc = 0.f;
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg) {
-      const int s = key0 + kg * 16;  // first key of the group; 16 | P keeps the group in one page
-      kb[kg] = zero8();
-      ksb[kg] = 127;
-      if (s < rows.len) {
-        int page = bt_row[s / P];
-        page = min(max(page, 0), a.num_pages - 1);
+      const int s = key0 + kg * 16;  // 16 | P keeps a group inside one page
+      ch.kb[kg] = zero8();
+      ch.ksb[kg] = 127;
+      if (s < len) {
+        const int page = __builtin_amdgcn_readlane(pg, 4 * slot + kg);
         const uint8_t *pb = a.base + int64_t(page) * a.page_stride;
-        const int e0 = s % P;
+        const int e0 = a.page_shift >= 0 ? s & (P - 1) : s % P;
         if (FMT == 0) {
           const uint8_t *p = pb + (e0 + n) * 128 + g * 16;
-          kb[kg] = cat(load16(p), load16(p + 64));
-          if (g == kg) scale_ptr = pb + P * 128 + 4 * (e0 + n);
+          ch.kb[kg] = cat(load16(p), load16(p + 64));
+          if (g == kg) ch.ksc = *reinterpret_cast<const float *>(pb + P * 128 + 4 * (e0 + n));
         } else {
           const int run_i = e0 >> 4;
           const v4i z = {0, 0, 0, 0};
-          kb[kg] = cat(load16(pb + run_i * 1024 + lane * 16), z);
-          ksb[kg] = pb[P * 64 + run_i * 64 + lane];
+          ch.kb[kg] = cat(load16(pb + run_i * 1024 + lane * 16), z);
+          ch.ksb[kg] = pb[P * 64 + run_i * 64 + lane];
         }
       }
     }
-    if (FMT == 0 && scale_ptr) ksc = *reinterpret_cast<const float *>(scale_ptr);
+  };
 
+  v8i qa[NR][HT];
+  float wv[NR][HT][4];
+  int qs[NR][HT];
+  int end[NR];
+  auto load_queries = [&](int b) {
+    row_ends<NR>(a, b, cap, end);
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const int64_t r = int64_t(b) * NR + j;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        const int h = ht * 16 + n;
+        if (h < a.H) {
+          if (FMT == 0) {
+            const uint8_t *p = a.q + (r * a.H + h) * 128 + g * 16;
+            qa[j][ht] = cat(load16(p), load16(p + 64));
+            qs[j][ht] = 0;
+          } else {
+            const uint8_t *p = a.q + (r * a.H + h) * 64 + g * 16;
+            const v4i z = {0, 0, 0, 0};
+            qa[j][ht] = cat(load16(p), z);
+            qs[j][ht] = (a.q_scale[r * a.H + h] >> (8 * g)) & 0xFF;
+          }
+        } else {
+          qa[j][ht] = zero8();
+          qs[j][ht] = 127;
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int hh = ht * 16 + 4 * g + jj;
+          wv[j][ht][jj] = hh < a.H ? a.w[r * a.H + hh] : 0.f;
+        }
+      }
+    }
+  };
+
+  auto score = [&](const Chunk<FMT> &ch, int b, int c) {
+    const int col = c * kChunk + lane;
     float res[NR];
 #pragma unroll
-    for (int j = 0; j < NR; ++j) res[j] = 0.f;
+    for (int j = 0; j < NR; ++j) {
+      float part[4];
 #pragma unroll
-    for (int kg = 0; kg < 4; ++kg) {
-#pragma unroll
-      for (int j = 0; j < NR; ++j) {
+      for (int kg = 0; kg < 4; ++kg) {
         float acc = 0.f;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
-          const v4f s = FMT == 0 ? mfma_fp8(qa[j][ht], kb[kg]) : mfma_fp4(qa[j][ht], kb[kg], qs[j][ht], ksb[kg]);
+          const v4f sc = FMT == 0 ? mfma_fp8(qa[j][ht], ch.kb[kg]) : mfma_fp4(qa[j][ht], ch.kb[kg], qs[j][ht], ch.ksb[kg]);
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) acc = fmaf(wv[j][ht][jj], fmaxf(s[jj], 0.f), acc);
+          for (int jj = 0; jj < 4; ++jj) acc = fmaf(wv[j][ht][jj], relu(sc[jj]), acc);
         }
-        acc = sum_row_groups(acc);
-        if (g == kg) res[j] = acc;
+        part[kg] = acc;
       }
+      res[j] = transpose_reduce4(part);
     }
-    const int col = key0 + lane;
     if (col < a.width) {
 #pragma unroll
       for (int j = 0; j < NR; ++j) {
-        const int64_t r = int64_t(b) * NR + j;
-        const float val = FMT == 0 ? res[j] * ksc : res[j];
-        a.logits[r * a.logits_row_stride + col] = col < rows.end[j] ? val : neg_inf();
+        const float val = FMT == 0 ? res[j] * ch.ksc : res[j];
+        a.logits[(int64_t(b) * NR + j) * a.logits_row_stride + col] = col < end[j] ? val : ninf;
       }
+    }
+  };
+
+  // ---- stream the share: chunk i+1 in flight while chunk i is scored ------------------
+  if (u0 < u1) {
+    int pg_base = u0;
+    int pg = load_pages(pg_base);
+    int b = find_seq(s_pref, a.B, u0);
+    int c = u0 - s_pref[b];
+    Chunk<FMT> bufA, bufB;
+    issue(bufA, pg, 0, b, c);
+    load_queries(b);
+    int qb = b;  // sequence whose queries are loaded
+    // next chunk's coordinates
+    auto advance = [&](int &bb, int &cc) {
+      if (++cc >= s_pref[bb + 1] - s_pref[bb]) {
+        bb = find_seq(s_pref, a.B, s_pref[bb + 1]);
+        cc = 0;
+      }
+    };
+    for (int u = u0; u < u1; u += 2) {
+      // chunk u in bufA (coordinates b, c); prefetch chunk u + 1 into bufB
+      int b1 = b, c1 = c;
+      const bool has1 = u + 1 < u1;
+      if (has1) {
+        advance(b1, c1);
+        if (u + 1 - pg_base >= 16) {
+          pg_base = u + 1;
+          pg = load_pages(pg_base);
+        }
+        issue(bufB, pg, u + 1 - pg_base, b1, c1);
+      }
+      if (b != qb) {
+        load_queries(b);
+        qb = b;
+      }
+      score(bufA, b, c);
+      if (!has1) break;
+      // chunk u + 1 in bufB; prefetch chunk u + 2 into bufA
+      int b2 = b1, c2 = c1;
+      const bool has2 = u + 2 < u1;
+      if (has2) {
+        advance(b2, c2);
+        if (u + 2 - pg_base >= 16) {
+          pg_base = u + 2;
+          pg = load_pages(pg_base);
+        }
+        issue(bufA, pg, u + 2 - pg_base, b2, c2);
+      }
+      if (b1 != qb) {
+        load_queries(b1);
+        qb = b1;
+      }
+      score(bufB, b1, c1);
+      b = b2;
+      c = c2;
     }
   }
 
-  // ---- -inf past each sequence's last chunk -------------------------------------
-  const int NU = (a.width + 255) / 256;
-  const int64_t R = int64_t(a.B) * NR;
-  const float ninf = neg_inf();
-  for (int64_t f = v; f < R * NU; f += V) {
-    const int64_t r = f / NU;
-    const int col = int(f % NU) * 256 + lane * 4;
-    const int bb = int(r / NR);
-    const int tail = (s_pref[bb + 1] - s_pref[bb]) * kChunk;
-    if (col >= tail && col < a.width) {
-      float *p = a.logits + r * a.logits_row_stride + col;
-      if (col + 4 <= a.width) {
-        *reinterpret_cast<v4f *>(p) = v4f{ninf, ninf, ninf, ninf};
-      } else {
-        for (int i = 0; col + i < a.width; ++i) p[i] = ninf;
-      }
-    }
-  }
 }
 
-template <int FMT, int HT>
-hipError_t launch_nr(const PagedArgs &a, dim3 grid, size_t lds, hipStream_t stream) {
-  switch (a.next_n) {
-    case 1: paged_logits_kernel<FMT, HT, 1><<<grid, kThreads, lds, stream>>>(a); break;
-    case 2: paged_logits_kernel<FMT, HT, 2><<<grid, kThreads, lds, stream>>>(a); break;
-    case 3: paged_logits_kernel<FMT, HT, 3><<<grid, kThreads, lds, stream>>>(a); break;
-    default: paged_logits_kernel<FMT, HT, 4><<<grid, kThreads, lds, stream>>>(a); break;
+// Persistent grid: as many workgroups as can be resident at once (a multiple of 8,
+// one equal slice per XCD), so every share starts immediately.
+template <int FMT, int HT, int NR>
+hipError_t launch_one(const PagedArgs &a, int num_cus, size_t lds, hipStream_t stream) {
+  // resident workgroups per CU for this kernel and LDS size, looked up once per size
+  static std::mutex mu;
+  static size_t cached_lds = ~size_t(0);
+  static int cached = 0;
+  int per_cu = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (cached_lds != lds) {
+      const hipError_t e =
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&cached, paged_logits_kernel<FMT, HT, NR>, kThreads, lds);
+      if (e != hipSuccess) return e;
+      cached_lds = lds;
+    }
+    per_cu = cached;
   }
+  const int nwg = max(8, (max(per_cu, 1) * num_cus) / 8 * 8);
+  paged_logits_kernel<FMT, HT, NR><<<dim3(nwg), kThreads, lds, stream>>>(a);
   return hipGetLastError();
 }
 
+template <int FMT, int HT>
+hipError_t launch_nr(const PagedArgs &a, int num_cus, size_t lds, hipStream_t stream) {
+  switch (a.next_n) {
+    case 1: return launch_one<FMT, HT, 1>(a, num_cus, lds, stream);
+    case 2: return launch_one<FMT, HT, 2>(a, num_cus, lds, stream);
+    case 3: return launch_one<FMT, HT, 3>(a, num_cus, lds, stream);
+    default: return launch_one<FMT, HT, 4>(a, num_cus, lds, stream);
+  }
+}
+
 template <int FMT>
-hipError_t launch_fmt(const PagedArgs &a, dim3 grid, size_t lds, hipStream_t stream) {
+hipError_t launch_fmt(const PagedArgs &a, int num_cus, size_t lds, hipStream_t stream) {
   const int ht = (a.H + 15) / 16;
-  if (ht <= 1) return launch_nr<FMT, 1>(a, grid, lds, stream);
-  if (ht <= 2) return launch_nr<FMT, 2>(a, grid, lds, stream);
-  if (ht <= 4) return launch_nr<FMT, 4>(a, grid, lds, stream);
-  return launch_nr<FMT, 8>(a, grid, lds, stream);
+  if (ht <= 1) return launch_nr<FMT, 1>(a, num_cus, lds, stream);
+  if (ht <= 2) return launch_nr<FMT, 2>(a, num_cus, lds, stream);
+  if (ht <= 4) return launch_nr<FMT, 4>(a, num_cus, lds, stream);
+  return launch_nr<FMT, 8>(a, num_cus, lds, stream);
 }
 
 }  // namespace
 
 hipError_t launch_paged_logits(const PagedArgs &a, int num_cus, hipStream_t stream) {
-  const int nwg = ((2 * num_cus + 7) / 8) * 8;
-  const size_t lds = size_t(a.B + 1) * sizeof(int);
-  const dim3 grid(nwg);
-  return a.fmt == 0 ? launch_fmt<0>(a, grid, lds, stream) : launch_fmt<1>(a, grid, lds, stream);
+  const size_t lds = size_t(2 * a.B + 1) * sizeof(int);
+  return a.fmt == 0 ? launch_fmt<0>(a, num_cus, lds, stream) : launch_fmt<1>(a, num_cus, lds, stream);
 }
 
 }  // namespace idx

@@ -1,23 +1,26 @@
 // Per-row top-k over [row_start, row_end): page
 // "vllm.v1.attention.ops.rocm_paged_mxfp4_indexer", _topk (-1 pads rows shorter than k).
 //
-// One workgroup of 1024 threads per row. Logits become order-preserving 32-bit keys
-// (-0.0 folded onto +0.0). A most-significant-digit-first radix select, 8 bits per
-// pass with per-wave LDS histograms, finds the k-th largest key T and how many
-// keys equal to T belong to the answer. A final pass in column order emits every
+// One workgroup per row. Logits become order-preserving 32-bit keys (-0.0 folded onto
+// +0.0). The row is read from global memory once: that pass keeps the keys in LDS
+// (when the row fits) and builds a histogram of their top 11 bits. The bin holding
+// the k-th largest key is found by a suffix scan over the 2048 bins; its keys - a
+// small set for any continuous distribution - are compacted into an LDS candidate
+// list, and two more radix digits (11 and 10 bits) over that list give the exact
+// k-th largest key T and how many keys equal to T complete the answer. When the
+// bin holds too many keys for the list (heavy ties), the two digits run over the
+// whole row instead. A last pass in column order, four keys per thread, emits every
 // key above T and the lowest-column ties, so the k indices come out in ascending
-// column order and equal values resolve to the lowest columns. Rows whose valid
-// range fits the LDS budget are read from global memory once and kept in LDS for
-// the remaining passes.
+// column order.
 #include "device.h"
 #include "launch.h"
 
 namespace idx {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
 constexpr int kMaxCache = 32768;  // keys kept in LDS (128 KiB)
+constexpr int kBins = 2048;       // first digit: 11 bits
+constexpr int kMaxCand = 4096;    // candidate list
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -30,11 +33,68 @@ __device__ __forceinline__ uint64_t lanes_below() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-__global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a, int cache_cap) {
+template <int NT>
+struct Smem {
+  uint32_t hist[kBins];
+  uint32_t cand[kMaxCand];
+  int wsum[NT / 64];
+  int sel_digit, sel_above, ncand;
+};
+
+// Exclusive prefix sum of v over the workgroup (thread order); *total gets the sum.
+template <int NT>
+__device__ int block_scan(int v, int *wsum, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int t = wsum[w];
+    if (w < wave) before += t;
+    all += t;
+  }
+  *total = all;
+  return before + x - v;
+}
+
+// Given counts per digit value in hist[0..nbins) (larger digit = larger key), find the
+// digit d with (# above d) < kr <= (# at or above d); writes sel_digit / sel_above.
+template <int NT>
+__device__ void select_digit(Smem<NT> &sm, int nbins, int kr) {
+  const int per = (nbins + NT - 1) / NT;  // bins per thread, walked from the top
+  const int top = nbins - 1 - threadIdx.x * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int d = top - i;
+    if (d >= 0) local += int(sm.hist[d]);
+  }
+  int total;
+  int run = block_scan<NT>(local, sm.wsum, &total);
+  for (int i = 0; i < per; ++i) {
+    const int d = top - i;
+    if (d < 0) break;
+    const int c = int(sm.hist[d]);
+    if (run < kr && run + c >= kr) {
+      sm.sel_digit = d;
+      sm.sel_above = run;
+    }
+    run += c;
+  }
+  __syncthreads();
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
   extern __shared__ uint32_t s_keys[];  // cache_cap keys
-  __shared__ uint32_t hist[kWaves][256];
-  __shared__ int s_digit, s_above;
-  __shared__ int s_cnt[kWaves][2];
+  __shared__ Smem<NT> sm;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -47,107 +107,112 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a, int cache_ca
   int32_t *out = a.out + int64_t(row) * a.out_row_stride;
 
   if (n <= k) {
-    for (int i = tid; i < k; i += kThreads) out[i] = i < n ? i : -1;
+    for (int i = tid; i < k; i += NT) out[i] = i < n ? i : -1;
     return;
   }
   const float *lr = a.logits + int64_t(row) * a.logits_row_stride + start;
   const bool cached = n <= cache_cap;
+  auto key_at = [&](int i) -> uint32_t { return cached ? s_keys[i] : order_key(lr[i]); };
 
-  uint32_t prefix = 0, pmask = 0;
-  int kr = k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < kWaves * 256; i += kThreads) (&hist[0][0])[i] = 0u;
+  // ---- pass 1: read the row, cache it, histogram of the top 11 bits ------------------
+  for (int i = tid; i < kBins; i += NT) sm.hist[i] = 0u;
+  if (tid == 0) sm.ncand = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += NT) {
+    const uint32_t key = order_key(lr[i]);
+    if (cached) s_keys[i] = key;
+    atomicAdd(&sm.hist[key >> 21], 1u);
+  }
+  __syncthreads();
+  select_digit<NT>(sm, kBins, k);
+  const uint32_t d1 = uint32_t(sm.sel_digit);
+  int kr = k - sm.sel_above;
+  const int c1 = int(sm.hist[d1]);
+
+  uint32_t T;  // the k-th largest key
+  if (c1 == kr) {
+    // the whole bin is selected: any key of the bin works as the cut, with all its
+    // keys taken; use the bin's lowest key so "above T or tie" selects exactly it
+    T = d1 << 21;
+    kr = n;  // every key equal to T is taken (there are at most c1 of them)
     __syncthreads();
-    for (int i = tid; i < n; i += kThreads) {
-      uint32_t key;
-      if (cached) {
-        if (pass == 0) {
-          key = order_key(lr[i]);
-          s_keys[i] = key;
-        } else {
-          key = s_keys[i];
+    // keys of bin d1 are >= T; "key > T" plus all ties == the whole bin
+  } else {
+    __syncthreads();
+    const bool use_cand = c1 <= kMaxCand;
+    if (use_cand) {
+      for (int i = tid; i < n; i += NT) {
+        const uint32_t key = key_at(i);
+        if ((key >> 21) == d1) sm.cand[atomicAdd(&sm.ncand, 1)] = key;
+      }
+    }
+    // digits 2 (bits 20..10) and 3 (bits 9..0)
+    uint32_t prefix = d1 << 21, pmask = 0xFFE00000u;
+#pragma unroll
+    for (int dg = 0; dg < 2; ++dg) {
+      const int shift = dg == 0 ? 10 : 0;
+      const int nb = dg == 0 ? 2048 : 1024;
+      for (int i = tid; i < kBins; i += NT) sm.hist[i] = 0u;
+      __syncthreads();
+      if (use_cand) {
+        const int nc = sm.ncand;
+        for (int i = tid; i < nc; i += NT) {
+          const uint32_t key = sm.cand[i];
+          if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> shift) & uint32_t(nb - 1)], 1u);
         }
       } else {
-        key = order_key(lr[i]);
-      }
-      if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // lane L owns digits 255-4L .. 252-4L (descending); find the digit d with
-      // (# keys above d) < kr <= (# keys at or above d)
-      int cnt[4];
-      int local = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 255 - 4 * lane - i;
-        int t = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) t += int(hist[w][d]);
-        cnt[i] = t;
-        local += t;
-      }
-      int incl = local;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      int running = incl - local;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (running < kr && running + cnt[i] >= kr) {
-          s_digit = 255 - 4 * lane - i;
-          s_above = running;
+        for (int i = tid; i < n; i += NT) {
+          const uint32_t key = key_at(i);
+          if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> shift) & uint32_t(nb - 1)], 1u);
         }
-        running += cnt[i];
       }
+      __syncthreads();
+      select_digit<NT>(sm, nb, kr);
+      prefix |= uint32_t(sm.sel_digit) << shift;
+      pmask |= uint32_t(nb - 1) << shift;
+      kr -= sm.sel_above;
+      __syncthreads();
     }
-    __syncthreads();
-    prefix |= uint32_t(s_digit) << shift;
-    pmask |= 255u << shift;
-    kr -= s_above;
-    __syncthreads();
+    T = prefix;
   }
 
-  // prefix is the k-th largest key; kr keys equal to it complete the answer
-  const uint32_t T = prefix;
+  // ---- ordered emission: 4 consecutive keys per thread per round ---------------------
   int run_eq = 0, run_sel = 0;
-  for (int base = 0; base < n && run_sel < k; base += kThreads) {
-    const int i = base + tid;
-    const bool in = i < n;
-    const uint32_t key = in ? (cached ? s_keys[i] : order_key(lr[i])) : 0u;
-    const bool gt = in && key > T;
-    const bool eq = in && key == T;
-    const uint64_t beq = __ballot(eq);
-    if (lane == 0) s_cnt[wave][0] = __popcll(beq);
-    __syncthreads();
-    int eq_before = run_eq, eq_all = run_eq;
+  for (int base = 0; base < n && run_sel < k; base += 4 * NT) {
+    const int i0 = base + 4 * tid;
+    uint32_t key[4];
+    int gt = 0, eq = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const int t = s_cnt[w][0];
-      if (w < wave) eq_before += t;
-      eq_all += t;
+    for (int j = 0; j < 4; ++j) {
+      key[j] = i0 + j < n ? key_at(i0 + j) : 0u;
+      const bool in = i0 + j < n;
+      gt += int(in && key[j] > T);
+      eq += int(in && key[j] == T);
     }
-    const int tie_rank = eq_before + __popcll(beq & lanes_below());
-    const bool sel = gt || (eq && tie_rank < kr);
-    const uint64_t bsel = __ballot(sel);
-    if (lane == 0) s_cnt[wave][1] = __popcll(bsel);
-    __syncthreads();
-    int sel_before = run_sel, sel_all = run_sel;
+    // exclusive prefixes of (gt, eq) in thread order; counts fit 16 bits each
+    int tot;
+    const int pre = block_scan<NT>(gt | (eq << 16), sm.wsum, &tot);
+    int eq_before = run_eq + (pre >> 16);
+    int pos = run_sel + (pre & 0xFFFF) + min(max(kr - run_eq, 0), pre >> 16);
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const int t = s_cnt[w][1];
-      if (w < wave) sel_before += t;
-      sel_all += t;
+    for (int j = 0; j < 4; ++j) {
+      if (i0 + j >= n) break;
+      bool sel = key[j] > T;
+      if (key[j] == T) {
+        sel = eq_before < kr;
+        ++eq_before;
+      }
+      if (sel) {
+        if (pos < k) out[pos] = i0 + j;
+        ++pos;
+      }
     }
-    const int pos = sel_before + __popcll(bsel & lanes_below());
-    if (sel && pos < k) out[pos] = i;
-    run_eq = eq_all;
-    run_sel = sel_all;
-    __syncthreads();
+    const int tot_gt = tot & 0xFFFF, tot_eq = tot >> 16;
+    run_sel += tot_gt + min(max(kr - run_eq, 0), tot_eq);
+    run_eq += tot_eq;
   }
+  (void)wave;
+  (void)lane;
 }
 
 }  // namespace
@@ -157,13 +222,19 @@ hipError_t launch_topk(const TopkArgs &a, int, hipStream_t stream) {
   const size_t lds = size_t(cap) * sizeof(uint32_t);
   static bool lds_raised = false;
   if (!lds_raised) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&topk_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             int(kMaxCache * sizeof(uint32_t)));
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&topk_kernel<1024>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxCache * sizeof(uint32_t)));
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&topk_kernel<256>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxCache * sizeof(uint32_t)));
     if (e != hipSuccess) return e;
     lds_raised = true;
   }
-  topk_kernel<<<dim3(a.rows), kThreads, lds, stream>>>(a, cap);
+  // few rows: the widest workgroup per row; many rows: narrower ones, more per CU
+  if (a.rows >= 1024)
+    topk_kernel<256><<<dim3(a.rows), 256, lds, stream>>>(a, cap);
+  else
+    topk_kernel<1024><<<dim3(a.rows), 1024, lds, stream>>>(a, cap);
   return hipGetLastError();
 }
 
