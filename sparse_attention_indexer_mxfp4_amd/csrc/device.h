@@ -56,6 +56,20 @@ __device__ __forceinline__ float transpose_reduce4(const float (&p)[4]) {
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
+// 4x4 transpose across the four 16-lane groups: on return r[i] in lane group g holds
+// what r[g] held in lane group i (same lane within the group). Two permlane32 swaps
+// then two permlane16 swaps, no arithmetic.
+__device__ __forceinline__ void transpose4(float (&r)[4]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(r[0]), __float_as_uint(r[2]), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(r[1]), __float_as_uint(r[3]), false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  r[0] = __uint_as_float(c[0]);
+  r[1] = __uint_as_float(c[1]);
+  r[2] = __uint_as_float(d[0]);
+  r[3] = __uint_as_float(d[1]);
+}
+
 __device__ __forceinline__ v4i load16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
 
 // max(x, 0) as one integer max on the bit pattern: negative floats are negative
@@ -139,5 +153,12 @@ __device__ __forceinline__ float e8m0_inv_scale(int b) {
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// e4m3fn (OCP) byte -> fp32, exact (NaN codes are not expected).
+__device__ __forceinline__ float dec_e4m3(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : float(m) * 0.001953125f;  // m * 2^-9
+  return (b & 0x80u) ? -mag : mag;
+}
 
 }  // namespace idx

@@ -9,9 +9,9 @@
 // list, and two more radix digits (11 and 10 bits) over that list give the exact
 // k-th largest key T and how many keys equal to T complete the answer. When the
 // bin holds too many keys for the list (heavy ties), the two digits run over the
-// whole row instead. A last pass in column order, four keys per thread, emits every
-// key above T and the lowest-column ties, so the k indices come out in ascending
-// column order.
+// whole row instead. A last pass in column order, several consecutive keys per thread
+// and one workgroup scan per 4096 keys, emits every key above T and the lowest-column
+// ties, so the k indices come out in ascending column order.
 #include "device.h"
 #include "launch.h"
 
@@ -20,7 +20,8 @@ namespace {
 
 constexpr int kMaxCache = 32768;  // keys kept in LDS (128 KiB)
 constexpr int kBins = 2048;       // first digit: 11 bits
-constexpr int kMaxCand = 4096;    // candidate list
+constexpr int kMaxCand = 2048;    // candidate list
+constexpr int kUnroll = 16;       // loads in flight per thread in the first pass
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -91,6 +92,48 @@ __device__ void select_digit(Smem<NT> &sm, int nbins, int kr) {
   __syncthreads();
 }
 
+// Ordered emission: KPT consecutive keys per thread per round. Writes every key above
+// T and the first kr keys equal to T, in column order, as out[pos] = column.
+template <int NT, int KPT, typename KeyAt>
+__device__ void emit(Smem<NT> &sm, KeyAt key_at, int n, int k, uint32_t T, int kr, int32_t *out) {
+  int run_eq = 0, run_sel = 0;
+  for (int base = 0; base < n && run_sel < k; base += KPT * NT) {
+    const int i0 = base + KPT * threadIdx.x;
+    uint32_t key[KPT];
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const bool in = i0 + j < n;
+      key[j] = in ? key_at(i0 + j) : 0u;
+      gt += int(in && key[j] > T);
+      eq += int(in && key[j] == T);
+    }
+    // exclusive prefixes of (gt, eq) in thread order; a round counts at most
+    // KPT * NT = 4096 keys, so each fits 16 bits
+    int tot;
+    const int pre = block_scan<NT>(gt | (eq << 16), sm.wsum, &tot);
+    int eq_before = run_eq + (pre >> 16);
+    int pos = run_sel + (pre & 0xFFFF) + min(max(kr - run_eq, 0), pre >> 16);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (i0 + j < n) {
+        bool sel = key[j] > T;
+        if (key[j] == T) {
+          sel = eq_before < kr;
+          ++eq_before;
+        }
+        if (sel) {
+          if (pos < k) out[pos] = i0 + j;
+          ++pos;
+        }
+      }
+    }
+    const int tot_gt = tot & 0xFFFF, tot_eq = tot >> 16;
+    run_sel += tot_gt + min(max(kr - run_eq, 0), tot_eq);
+    run_eq += tot_eq;
+  }
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
   extern __shared__ uint32_t s_keys[];  // cache_cap keys
@@ -115,13 +158,27 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
   auto key_at = [&](int i) -> uint32_t { return cached ? s_keys[i] : order_key(lr[i]); };
 
   // ---- pass 1: read the row, cache it, histogram of the top 11 bits ------------------
+  // kUnroll independent loads per thread are issued before any of them is used, so a
+  // batch costs one memory round trip
   for (int i = tid; i < kBins; i += NT) sm.hist[i] = 0u;
   if (tid == 0) sm.ncand = 0;
   __syncthreads();
-  for (int i = tid; i < n; i += NT) {
-    const uint32_t key = order_key(lr[i]);
-    if (cached) s_keys[i] = key;
-    atomicAdd(&sm.hist[key >> 21], 1u);
+  for (int base = 0; base < n; base += kUnroll * NT) {
+    float x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = base + u * NT + tid;
+      x[u] = i < n ? lr[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = base + u * NT + tid;
+      if (i < n) {
+        const uint32_t key = order_key(x[u]);
+        if (cached) s_keys[i] = key;
+        atomicAdd(&sm.hist[key >> 21], 1u);
+      }
+    }
   }
   __syncthreads();
   select_digit<NT>(sm, kBins, k);
@@ -176,43 +233,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
     T = prefix;
   }
 
-  // ---- ordered emission: 4 consecutive keys per thread per round ---------------------
-  int run_eq = 0, run_sel = 0;
-  for (int base = 0; base < n && run_sel < k; base += 4 * NT) {
-    const int i0 = base + 4 * tid;
-    uint32_t key[4];
-    int gt = 0, eq = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      key[j] = i0 + j < n ? key_at(i0 + j) : 0u;
-      const bool in = i0 + j < n;
-      gt += int(in && key[j] > T);
-      eq += int(in && key[j] == T);
-    }
-    // exclusive prefixes of (gt, eq) in thread order; counts fit 16 bits each
-    int tot;
-    const int pre = block_scan<NT>(gt | (eq << 16), sm.wsum, &tot);
-    int eq_before = run_eq + (pre >> 16);
-    int pos = run_sel + (pre & 0xFFFF) + min(max(kr - run_eq, 0), pre >> 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (i0 + j >= n) break;
-      bool sel = key[j] > T;
-      if (key[j] == T) {
-        sel = eq_before < kr;
-        ++eq_before;
-      }
-      if (sel) {
-        if (pos < k) out[pos] = i0 + j;
-        ++pos;
-      }
-    }
-    const int tot_gt = tot & 0xFFFF, tot_eq = tot >> 16;
-    run_sel += tot_gt + min(max(kr - run_eq, 0), tot_eq);
-    run_eq += tot_eq;
-  }
-  (void)wave;
-  (void)lane;
+  // ---- ordered emission ---------------------------------------------------------------
+  if (cached)
+    emit<NT, 4096 / NT>(sm, [&](int i) { return s_keys[i]; }, n, k, T, kr, out);
+  else
+    emit<NT, 4>(sm, [&](int i) { return order_key(lr[i]); }, n, k, T, kr, out);
 }
 
 }  // namespace
