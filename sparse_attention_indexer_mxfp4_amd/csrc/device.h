@@ -9,6 +9,7 @@ namespace idx {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------------
 // Matrix cores: v_mfma_f32_16x16x128_f8f6f4 (gfx950), one 16x16 output tile with a
@@ -72,10 +73,44 @@ __device__ __forceinline__ void transpose4(float (&r)[4]) {
 
 __device__ __forceinline__ v4i load16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
 
+// ---------------------------------------------------------------------------------
+// Buffer memory operations: a 128-bit resource (base address, size in bytes) held in
+// scalar registers. An access whose byte offset is not below the size touches no
+// memory: a load returns zeros and a store is dropped. Range checks cost nothing
+// and leave the code free of branches.
+// ---------------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t buffer_rsrc;
+
+// a byte count clamped to what a resource can describe
+__device__ __forceinline__ uint32_t range_bytes(int64_t bytes) {
+  return bytes <= 0 ? 0u : (bytes >= int64_t(0x7FFFFFFF) ? 0x7FFFFFFFu : uint32_t(bytes));
+}
+
+__device__ __forceinline__ buffer_rsrc make_rsrc(const void *base, uint32_t bytes) {
+  // dword 3: raw (untyped) 32-bit access, the value the gfx9 family expects
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, int(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ v4i buffer_load16(buffer_rsrc r, uint32_t off) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ float buffer_load_f32(buffer_rsrc r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void buffer_store_f32(float x, buffer_rsrc r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+}
+
 // max(x, 0) as one integer max on the bit pattern: negative floats are negative
 // integers, so they (and -0.0) become +0.0 and non-negative floats pass unchanged.
 // fmaxf would first canonicalise its input (a second VALU op) under IEEE mode.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Makes x a value produced at this point of the program (an empty asm statement that
+// reads and writes it): the computation of x can no longer be moved past it.
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 
 // A value the compiler may treat as wavefront-uniform (kept in a scalar register).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }

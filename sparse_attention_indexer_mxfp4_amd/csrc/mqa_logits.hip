@@ -6,8 +6,9 @@
 // sum instead of once per head.
 //
 // The contraction runs on the fp8 matrix cores; what limits it on gfx950 is the
-// per-element epilogue, because the VALU and the matrix core barely overlap: a ReLU
-// plus a multiply-add per (t, h, s) costs as much time as the MFMA that produced it.
+// per-element epilogue, because the VALU and the matrix core overlap only partly (an
+// MFMA holds off vector issue for most of its cycles): a ReLU plus a multiply-add per
+// (t, h, s) costs as much time as the MFMA that produced it.
 // The kernel therefore uses max(x, 0) = (x + |x|) / 2:
 //
 //   sum_h w_h max(S_h, 0) = 1/2 * ( sum_h w_h |S_h|  +  sum_h w_h S_h ).
@@ -53,6 +54,20 @@ __device__ void fill_neg_inf(float *row, int from, int to, int lane) {
     } else {
       for (int i = 0; i < 4 && c + i < to; ++i) row[c + i] = ninf;
     }
+  }
+}
+
+// One step of a reduce-scatter over the 16 lanes of a DPP row. x[0..2*HALF) holds
+// partial sums; the DPP control pairs each lane with one that differs in the bit
+// `upper` tests (and possibly lower bits). The lane keeps the half selected by that
+// bit, adds the partner's copy of the same half, and on return x[0..HALF) holds it.
+template <int CTRL, int HALF>
+__device__ __forceinline__ void reduce_scatter_step(float (&x)[32], bool upper) {
+#pragma unroll
+  for (int j = 0; j < HALF; ++j) {
+    const float keep = upper ? x[j + HALF] : x[j];
+    const float send = upper ? x[j] : x[j + HALF];
+    x[j] = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), CTRL, 0xF, 0xF, false));
   }
 }
 
@@ -123,9 +138,9 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
     }
 
     // qt[d] = sum_h w[h] q[h, d], from the query bytes already in registers: lane
-    // (g, n) holds heads ht*16 + n of K-group g; sum its HT heads, then the 16 lanes of
-    // its row with DPP rotations, and keep the two of group g's 32 channels this lane
-    // writes out: i = 2n, 2n+1.
+    // (g, n) holds head ht*16 + n's 32 channels of K-group g for every ht. Convert them
+    // two per instruction, accumulate over ht, then sum over the 16 head lanes with a
+    // reduce-scatter that leaves channels 2n, 2n+1 of the group in lane n.
     float pq[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) pq[i] = 0.f;
@@ -134,25 +149,20 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
       const int h = ht * 16 + n;
       const float wh = (active[rr] && h < a.H) ? a.w[int64_t(r) * a.w_row_stride + h] : 0.f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) pq[i] = fmaf(wh, dec_e4m3((uint32_t(qa[rr][ht][i >> 2]) >> (8 * (i & 3))) & 0xFFu), pq[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      float x = pq[i];
-      x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror:8
-      x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));  // row_ror:4
-      x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));  // row_ror:2
-      x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));  // row_ror:1
-      pq[i] = x;
-    }
-    float q0 = pq[0], q1 = pq[1];
-#pragma unroll
-    for (int i = 2; i < 32; i += 2) {
-      if (n == i / 2) {
-        q0 = pq[i];
-        q1 = pq[i + 1];
+      for (int wd = 0; wd < 8; ++wd) {
+        const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(qa[rr][ht][wd], false);
+        const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(qa[rr][ht][wd], true);
+        pq[4 * wd + 0] = fmaf(wh, lo[0], pq[4 * wd + 0]);
+        pq[4 * wd + 1] = fmaf(wh, lo[1], pq[4 * wd + 1]);
+        pq[4 * wd + 2] = fmaf(wh, hi[0], pq[4 * wd + 2]);
+        pq[4 * wd + 3] = fmaf(wh, hi[1], pq[4 * wd + 3]);
       }
     }
+    reduce_scatter_step<0x140, 16>(pq, n & 8);  // row_mirror: partner differs in bit 3
+    reduce_scatter_step<0x141, 8>(pq, n & 4);   // row_half_mirror: bits 0..2
+    reduce_scatter_step<0x1B, 4>(pq, n & 2);    // quad_perm [3,2,1,0]: bits 0, 1
+    reduce_scatter_step<0xB1, 2>(pq, n & 1);    // quad_perm [1,0,3,2]: bit 0
+    const float q0 = pq[0], q1 = pq[1];
     // byte offset of channels 2n, 2n+1 of K-group g
     const int qoff = n < 8 ? 16 * g + 2 * n : 64 + 16 * g + 2 * (n - 8);
     float m = fmaxf(fabsf(q0), fabsf(q1));
@@ -163,12 +173,16 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
     const float inv = __uint_as_float(uint32_t(max(min(7 - ex + 127, 254), 1)) << 23);
     lscale[rr] = __uint_as_float(uint32_t(max(min(ex - 7 + 127, 254), 1)) << 23);
     float x0 = q0 * inv, x1 = q1 * inv;
+    // |x| < 256 after the scaling, inside the e4m3 range: each part is the
+    // round-to-nearest-even e4m3 value of what the previous parts left, and the
+    // remainder after subtracting it is exact in fp32
 #pragma unroll
     for (int part = 0; part < 4; ++part) {
-      const uint32_t e0 = enc_e4m3(x0), e1 = enc_e4m3(x1);
-      x0 -= dec_e4m3(e0);
-      x1 -= dec_e4m3(e1);
-      *reinterpret_cast<uint16_t *>(&sl[wave][(rr * 4 + part) * kKeyStride + qoff]) = uint16_t(e0 | (e1 << 8));
+      const int e = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+      const v2f d = __builtin_amdgcn_cvt_pk_f32_fp8(e, false);
+      x0 -= d[0];
+      x1 -= d[1];
+      *reinterpret_cast<uint16_t *>(&sl[wave][(rr * 4 + part) * kKeyStride + qoff]) = uint16_t(e);
     }
   }
   // rows 8..15 of the qt operand tile stay zero
@@ -200,19 +214,25 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
   // K chunks stream through two LDS buffers. The global loads of chunk i+2 are issued
   // while chunk i is scored and staged into LDS a whole iteration later, so a load has
   // two chunks of scoring to arrive in; one barrier per chunk hands a buffer over.
+  // Loads and stores are buffer operations with hardware range checks (keys past N
+  // read as zero, columns past the WG's range or rows past M are dropped), so the
+  // loop has no data-dependent branches and the memory counter waits at the staging
+  // step cover only the chunk being staged.
   struct Fetch {
     v4i kv[2];
     float ks;
   };
   auto fetch = [&](Fetch &f, int c) {
+    const int64_t left = max(int64_t(a.N) - c, int64_t(0));
+    const buffer_rsrc kr = make_rsrc(a.k + int64_t(c) * a.k_row_stride, range_bytes(left * a.k_row_stride));
+    const buffer_rsrc sr = make_rsrc(a.k_scale + c, range_bytes(left * 4));
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int idx = tid + 256 * i;
       const int key = idx >> 3, part = idx & 7;
-      f.kv[i] = v4i{0, 0, 0, 0};
-      if (c + key < a.N) f.kv[i] = load16(a.k + int64_t(c + key) * a.k_row_stride + part * 16);
+      f.kv[i] = buffer_load16(kr, uint32_t(key * a.k_row_stride + part * 16));
     }
-    f.ks = (tid < kChunk && c + tid < a.N) ? a.k_scale[c + tid] : 0.f;
+    f.ks = buffer_load_f32(sr, uint32_t((tid & (kChunk - 1)) * 4));
   };
   auto stage = [&](const Fetch &f, int buf) {
 #pragma unroll
@@ -224,6 +244,18 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
     if (tid < kChunk) ss[buf][tid] = f.ks;
   };
 
+  // one store range per row: [0, c_end) of the row for rows that exist, nothing else
+  buffer_rsrc orow[kRowsPerWave];
+#pragma unroll
+  for (int rr = 0; rr < kRowsPerWave; ++rr)
+    orow[rr] = make_rsrc(a.logits + int64_t(active[rr] ? r_base + rr : 0) * a.logits_row_stride,
+                         active[rr] ? uint32_t(c_end) * 4u : 0u);
+
+  // Scoring of one chunk as a fixed schedule: the MFMAs of key group kg+1 are issued
+  // one at a time, each followed by the |S| multiply-adds of one (row, head tile) of
+  // group kg, whose MFMA was issued a whole group earlier. Scheduling fences keep the
+  // compiler from regrouping them, so the matrix core always has work queued while the
+  // VALU runs.
   auto score = [&](int c, int buf) {
     v8i kb[4];
 #pragma unroll
@@ -231,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
       const uint8_t *kp = &sk[buf][(kg * 16 + n) * kKeyStride + g * 16];
       kb[kg] = cat(*reinterpret_cast<const v4i *>(kp), *reinterpret_cast<const v4i *>(kp + 64));
     }
-    float part[kRowsPerWave][4];  // sum over this lane's 16 heads of w * |S|
+    float part[kRowsPerWave][4];  // sum over this lane's heads of w * |S|, per key group
     float lin[4];                 // qt . k for row g of the wave (g < 2), before the 2^e scale
     v4f sv[2][kRowsPerWave][HT];
     v4f lv[2];
@@ -243,33 +275,24 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg) {
-      if (kg < 3) {
+      const int cur = kg & 1, nxt = cur ^ 1;
+      float acc[kRowsPerWave];
 #pragma unroll
-        for (int rr = 0; rr < kRowsPerWave; ++rr)
+      for (int rr = 0; rr < kRowsPerWave; ++rr) acc[rr] = 0.f;
 #pragma unroll
-          for (int ht = 0; ht < HT; ++ht) sv[(kg + 1) & 1][rr][ht] = mfma_fp8(qa[rr][ht], kb[kg + 1]);
-        lv[(kg + 1) & 1] = mfma_fp8(la, kb[kg + 1]);
+      for (int u = 0; u < kRowsPerWave * HT; ++u) {
+        const int rr = u % kRowsPerWave, ht = u / kRowsPerWave;
+        if (kg < 3) sv[nxt][rr][ht] = mfma_fp8(qa[rr][ht], kb[(kg + 1) & 3]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[rr] = fmaf(wv[rr][ht][j], fabsf(sv[cur][rr][ht][j]), acc[rr]);
+        pin(acc[rr]);  // computed here, not sunk towards its use
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int rr = 0; rr < kRowsPerWave; ++rr) {
-        float acc = 0.f;
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc = fmaf(wv[rr][ht][j], fabsf(sv[kg & 1][rr][ht][j]), acc);
-        part[rr][kg] = acc;
-      }
-      const v4f l4 = lv[kg & 1];
+      if (kg < 3) lv[nxt] = mfma_fp8(la, kb[(kg + 1) & 3]);
+      const v4f l4 = lv[cur];
       lin[kg] = (l4[0] + l4[1]) + (l4[2] + l4[3]);
-      // within this fenced region no VALU op reads an MFMA issued in it: one MFMA,
-      // then a run of VALU ops, repeated, keeps both units fed
-      if (kg < 3) {
 #pragma unroll
-        for (int i = 0; i < kRowsPerWave * HT + 1; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        }
-      }
+      for (int rr = 0; rr < kRowsPerWave; ++rr) part[rr][kg] = acc[rr];
       __builtin_amdgcn_sched_barrier(0);
     }
     // lane L: |S| sums for key L of each row; qt . k for key L of rows 0 and 1
@@ -278,11 +301,10 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
     const float sc = 0.5f * ss[buf][lane];
 #pragma unroll
     for (int rr = 0; rr < kRowsPerWave; ++rr) {
-      const float val = (transpose_reduce4(part[rr]) + lin[rr] * lscale[rr]) * sc;
-      if (active[rr] && col < c_end) {
-        const int r = r_base + rr;
-        a.logits[int64_t(r) * a.logits_row_stride + col] = (col >= rlo[rr] && col < rhi[rr]) ? val : neg_inf();
-      }
+      float val = (transpose_reduce4(part[rr]) + lin[rr] * lscale[rr]) * sc;
+      pin(val);  // a select below, not a branch around the arithmetic
+      const float out = (col >= rlo[rr] && col < rhi[rr]) ? val : neg_inf();
+      buffer_store_f32(out, orow[rr], uint32_t(col) * 4u);
     }
   };
 
@@ -290,7 +312,7 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
   if (c0 < c_end) {
     fetch(fa, c0);
     stage(fa, 0);
-    if (c0 + kChunk < c_end) fetch(fa, c0 + kChunk);
+    fetch(fa, c0 + kChunk);
   }
   __syncthreads();
   // invariant at the top of a step: buffer `buf` holds chunk c, the loads of chunk
@@ -298,16 +320,16 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
   int buf = 0;
   for (int c = c0; c < c_end; c += 2 * kChunk) {
     // chunk c (in flight: c + 64 in fa)
-    if (c + 2 * kChunk < c_end) fetch(fb, c + 2 * kChunk);
+    fetch(fb, c + 2 * kChunk);
     score(c, buf);
-    if (c + kChunk < c_end) stage(fa, buf ^ 1);
+    stage(fa, buf ^ 1);
     __syncthreads();
     buf ^= 1;
     if (c + kChunk >= c_end) break;
     // chunk c + 64 (in flight: c + 128 in fb)
-    if (c + 3 * kChunk < c_end) fetch(fa, c + 3 * kChunk);
+    fetch(fa, c + 3 * kChunk);
     score(c + kChunk, buf);
-    if (c + 2 * kChunk < c_end) stage(fb, buf ^ 1);
+    stage(fb, buf ^ 1);
     __syncthreads();
     buf ^= 1;
   }
