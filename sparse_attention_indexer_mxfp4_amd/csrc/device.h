@@ -103,6 +103,12 @@ __device__ __forceinline__ void buffer_store_f32(float x, buffer_rsrc r, uint32_
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
 }
 
+// Streaming store (non-temporal cache policy): output that is not read again by the
+// kernel should not push reusable lines (K tiles) out of L2.
+__device__ __forceinline__ void buffer_store_f32_nt(float x, buffer_rsrc r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 2);
+}
+
 // max(x, 0) as one integer max on the bit pattern: negative floats are negative
 // integers, so they (and -0.0) become +0.0 and non-negative floats pass unchanged.
 // fmaxf would first canonicalise its input (a second VALU op) under IEEE mode.

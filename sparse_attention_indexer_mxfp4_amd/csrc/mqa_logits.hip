@@ -43,6 +43,7 @@ constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 2;
 constexpr int kRowsPerWG = kWaves * kRowsPerWave;
 constexpr int kChunk = 64;
+constexpr int kDepth = 2;  // K chunks requested ahead of the one being scored
 constexpr int kKeyStride = 144;  // LDS bytes per key / query row: 128 + 16 of padding against bank conflicts
 
 // -inf into row[from, to); `from` is a multiple of 4 and the row is 16-byte aligned.
@@ -50,9 +51,9 @@ __device__ void fill_neg_inf(float *row, int from, int to, int lane) {
   const float ninf = neg_inf();
   for (int c = from + 4 * lane; c < to; c += 256) {
     if (c + 4 <= to) {
-      *reinterpret_cast<v4f *>(row + c) = v4f{ninf, ninf, ninf, ninf};
+      __builtin_nontemporal_store(v4f{ninf, ninf, ninf, ninf}, reinterpret_cast<v4f *>(row + c));
     } else {
-      for (int i = 0; i < 4 && c + i < to; ++i) row[c + i] = ninf;
+      for (int i = 0; i < 4 && c + i < to; ++i) __builtin_nontemporal_store(ninf, row + c + i);
     }
   }
 }
@@ -211,9 +212,10 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
     }
   }
 
-  // K chunks stream through two LDS buffers. The global loads of chunk i+2 are issued
-  // while chunk i is scored and staged into LDS a whole iteration later, so a load has
-  // two chunks of scoring to arrive in; one barrier per chunk hands a buffer over.
+  // K chunks stream through two LDS buffers, fed from kDepth sets of registers: the
+  // global loads of chunk i+kDepth are issued while chunk i is scored and staged after
+  // chunk i+kDepth-1 is scored, so a load has kDepth chunks of scoring to arrive in;
+  // one barrier per chunk hands a buffer over.
   // Loads and stores are buffer operations with hardware range checks (keys past N
   // read as zero, columns past the WG's range or rows past M are dropped), so the
   // loop has no data-dependent branches and the memory counter waits at the staging
@@ -304,34 +306,31 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
       float val = (transpose_reduce4(part[rr]) + lin[rr] * lscale[rr]) * sc;
       pin(val);  // a select below, not a branch around the arithmetic
       const float out = (col >= rlo[rr] && col < rhi[rr]) ? val : neg_inf();
-      buffer_store_f32(out, orow[rr], uint32_t(col) * 4u);
+      buffer_store_f32_nt(out, orow[rr], uint32_t(col) * 4u);
     }
   };
 
-  Fetch fa, fb;
+  Fetch f[kDepth];
   if (c0 < c_end) {
-    fetch(fa, c0);
-    stage(fa, 0);
-    fetch(fa, c0 + kChunk);
+    fetch(f[0], c0);
+    stage(f[0], 0);
+#pragma unroll
+    for (int u = 1; u < kDepth; ++u) fetch(f[u], c0 + u * kChunk);
   }
   __syncthreads();
-  // invariant at the top of a step: buffer `buf` holds chunk c, the loads of chunk
-  // c + 64 are in flight in one Fetch set
   int buf = 0;
-  for (int c = c0; c < c_end; c += 2 * kChunk) {
-    // chunk c (in flight: c + 64 in fa)
-    fetch(fb, c + 2 * kChunk);
-    score(c, buf);
-    stage(fa, buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    if (c + kChunk >= c_end) break;
-    // chunk c + 64 (in flight: c + 128 in fb)
-    fetch(fa, c + 3 * kChunk);
-    score(c + kChunk, buf);
-    stage(fb, buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+  for (int c = c0; c < c_end; c += kDepth * kChunk) {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      // buffer `buf` holds chunk cc; set u is free, set (u + 1) % kDepth holds cc + 64
+      const int cc = c + u * kChunk;
+      if (cc >= c_end) break;
+      fetch(f[u], cc + kDepth * kChunk);
+      score(cc, buf);
+      stage(f[(u + 1) % kDepth], buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
   }
 }
 
