@@ -1,17 +1,25 @@
 // Per-row top-k over [row_start, row_end): page
 // "vllm.v1.attention.ops.rocm_paged_mxfp4_indexer", _topk (-1 pads rows shorter than k).
 //
-// One workgroup per row. Logits become order-preserving 32-bit keys (-0.0 folded onto
-// +0.0). The row is read from global memory once: that pass keeps the keys in LDS
-// (when the row fits) and builds a histogram of their top 11 bits. The bin holding
-// the k-th largest key is found by a suffix scan over the 2048 bins; its keys - a
-// small set for any continuous distribution - are compacted into an LDS candidate
-// list, and two more radix digits (11 and 10 bits) over that list give the exact
-// k-th largest key T and how many keys equal to T complete the answer. When the
-// bin holds too many keys for the list (heavy ties), the two digits run over the
-// whole row instead. A last pass in column order, several consecutive keys per thread
-// and one workgroup scan per 4096 keys, emits every key above T and the lowest-column
-// ties, so the k indices come out in ascending column order.
+// One workgroup per row; logits become order-preserving 32-bit keys (-0.0 folded onto
+// +0.0). The k-th largest key T is found by a three-digit radix select (11, 11 and 10
+// bits) and the answer is every key above T plus the lowest-column keys equal to T,
+// written in ascending column order. The kernel is a short chain of phases, each
+// cheap in latency:
+//   1. one read of the row from global memory: keys into LDS (rows up to kMaxCache)
+//      and a histogram of the top 11 bits;
+//   2. wave 0 alone finds the bin of the k-th key (lane sums of 32 bins, a DPP lane
+//      scan, one lane walks its bins in registers), then one barrier;
+//   3. each wave walks its own contiguous segment of the row: it counts the keys in
+//      higher bins, compacts the keys of the selected bin into a candidate list (one
+//      LDS atomic per wave and step) tagged with the wave's number, and histograms
+//      their next 11 bits;
+//   4. digits 2 and 3 are selected over the candidates, and each candidate above or
+//      equal to T is counted against its wave;
+//   5. every wave then knows how many selected keys precede its segment and walks it
+//      once more, placing the selected keys with ballots and lane-prefix counts.
+// If the selected bin holds more keys than the candidate list (heavy ties), digit 3
+// and the per-wave counts come from extra passes over the row instead.
 #include "device.h"
 #include "launch.h"
 
@@ -19,8 +27,7 @@ namespace idx {
 namespace {
 
 constexpr int kMaxCache = 32768;  // keys kept in LDS (128 KiB)
-constexpr int kBins = 2048;       // first digit: 11 bits
-constexpr int kMaxCand = 2048;    // candidate list
+constexpr int kBins = 2048;       // digits 1 and 2: 11 bits; digit 3: 10 bits
 constexpr int kUnroll = 16;       // loads in flight per thread in the first pass
 
 __device__ __forceinline__ uint32_t order_key(float x) {
@@ -29,108 +36,254 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t lanes_below() {
-  const int lane = threadIdx.x & 63;
-  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+__device__ __forceinline__ int lane_prefix(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
 }
 
+// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS traffic): shifts of
+// 1, 2, 4 and 8 lanes inside each 16-lane row, then the last lane of rows 0 and 2
+// broadcast into rows 1 and 3, and lane 31 into rows 2 and 3. Lanes a move does not
+// reach add 0.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum(int x) { return __builtin_amdgcn_readlane(wave_incl_scan(x), 63); }
+
+// Candidate list size: long rows (few rows, 1024 threads) get more room.
 template <int NT>
-struct Smem {
-  uint32_t hist[kBins];
-  uint32_t cand[kMaxCand];
-  int wsum[NT / 64];
+struct Cfg {
+  static constexpr int kCand = NT >= 1024 ? 2048 : 1024;
+  static constexpr int kWaves = NT / 64;
+};
+
+template <int NT>
+struct __attribute__((aligned(16))) Smem {
+  uint32_t hist[kBins];           // digit 1, then digit 3
+  uint32_t hist2[kBins];          // digit 2
+  uint32_t cand[Cfg<NT>::kCand];  // (wave << 21) | low 21 bits of a key of the selected bin
+  int wgt[Cfg<NT>::kWaves];       // per wave segment: keys above T
+  int weq[Cfg<NT>::kWaves];       // per wave segment: keys equal to T
   int sel_digit, sel_above, ncand;
 };
 
-// Exclusive prefix sum of v over the workgroup (thread order); *total gets the sum.
-template <int NT>
-__device__ int block_scan(int v, int *wsum, int *total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
+// Wave 0 finds the digit d with (# keys above d) < kr <= (# at or above d) in
+// hist[0..NBINS) (larger digit = larger key) and publishes d and the count above
+// it; the barrier makes them visible to the workgroup. Each lane loads its NBINS/64
+// bins once and walks them in registers.
+template <int NT, int NBINS>
+__device__ void select_digit(Smem<NT> &sm, const uint32_t *hist, int kr) {
+  static_assert(NBINS % 256 == 0, "whole 16-byte loads per lane");
+  constexpr int kPer = NBINS / 64;
+  if ((threadIdx.x >> 6) == 0) {
+    const int lane = threadIdx.x & 63;
+    const int first = NBINS - (lane + 1) * kPer;  // this lane: bins [first, first + kPer), lane 0 highest
+    int c[kPer];
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  __syncthreads();
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  int before = 0, all = 0;
+    for (int q = 0; q < kPer / 4; ++q) {
+      const v4i x = *reinterpret_cast<const v4i *>(hist + first + 4 * q);
+      c[4 * q] = x[0];
+      c[4 * q + 1] = x[1];
+      c[4 * q + 2] = x[2];
+      c[4 * q + 3] = x[3];
+    }
+    int local = 0;
 #pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    const int t = wsum[w];
-    if (w < wave) before += t;
-    all += t;
-  }
-  *total = all;
-  return before + x - v;
-}
-
-// Given counts per digit value in hist[0..nbins) (larger digit = larger key), find the
-// digit d with (# above d) < kr <= (# at or above d); writes sel_digit / sel_above.
-template <int NT>
-__device__ void select_digit(Smem<NT> &sm, int nbins, int kr) {
-  const int per = (nbins + NT - 1) / NT;  // bins per thread, walked from the top
-  const int top = nbins - 1 - threadIdx.x * per;
-  int local = 0;
-  for (int i = 0; i < per; ++i) {
-    const int d = top - i;
-    if (d >= 0) local += int(sm.hist[d]);
-  }
-  int total;
-  int run = block_scan<NT>(local, sm.wsum, &total);
-  for (int i = 0; i < per; ++i) {
-    const int d = top - i;
-    if (d < 0) break;
-    const int c = int(sm.hist[d]);
-    if (run < kr && run + c >= kr) {
+    for (int j = 0; j < kPer; ++j) local += c[j];
+    const int incl = wave_incl_scan(local);
+    int run = incl - local;
+    if (run < kr && incl >= kr) {
+      int d = first, above = run;
+      bool found = false;
+#pragma unroll
+      for (int j = kPer - 1; j >= 0; --j) {
+        if (!found && run + c[j] >= kr) {
+          found = true;
+          d = first + j;
+          above = run;
+        }
+        run += c[j];
+      }
       sm.sel_digit = d;
-      sm.sel_above = run;
+      sm.sel_above = above;
     }
-    run += c;
   }
   __syncthreads();
 }
 
-// Ordered emission: KPT consecutive keys per thread per round. Writes every key above
-// T and the first kr keys equal to T, in column order, as out[pos] = column.
-template <int NT, int KPT, typename KeyAt>
-__device__ void emit(Smem<NT> &sm, KeyAt key_at, int n, int k, uint32_t T, int kr, int32_t *out) {
-  int run_eq = 0, run_sel = 0;
-  for (int base = 0; base < n && run_sel < k; base += KPT * NT) {
-    const int i0 = base + KPT * threadIdx.x;
-    uint32_t key[KPT];
-    int gt = 0, eq = 0;
+// This wave's contiguous segment [lo, hi) of the row: equal shares, whole steps.
+template <int NT, int KPL>
+__device__ __forceinline__ void segment(int n, int wave, int &lo, int &hi) {
+  constexpr int kStep = 64 * KPL;
+  const int seg = (n + Cfg<NT>::kWaves * kStep - 1) / (Cfg<NT>::kWaves * kStep) * kStep;
+  lo = min(n, wave * seg);
+  hi = min(n, lo + seg);
+}
+
+// Phases 3 to 5 for one row, with the keys read through key_at (LDS or global) and
+// KPL keys per lane in flight per step.
+template <int NT, int KPL, typename KeyAt>
+__device__ void finish_row(Smem<NT> &sm, KeyAt key_at, int n, int k, int32_t *out) {
+  constexpr int kStep = 64 * KPL;
+  constexpr int kCand = Cfg<NT>::kCand;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int lo, hi;
+  segment<NT, KPL>(n, wave, lo, hi);
+
+  const uint32_t d1 = uint32_t(sm.sel_digit);
+  int kr = k - sm.sel_above;  // keys still needed from bin d1
+  const int c1 = int(sm.hist[d1]);
+  const bool whole_bin = c1 == kr;
+  const bool use_cand = !whole_bin && c1 <= kCand;
+  __syncthreads();  // every thread has read hist before it is cleared below
+
+  // ---- phase 3: per-segment counts, candidates, digit-2 histogram --------------------
+  for (int i = tid; i < kBins; i += NT) sm.hist[i] = 0u;
+  int above = 0, match = 0;
+  for (int base = lo; base < hi; base += kStep) {
+    uint32_t key[KPL];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const bool in = i0 + j < n;
-      key[j] = in ? key_at(i0 + j) : 0u;
-      gt += int(in && key[j] > T);
-      eq += int(in && key[j] == T);
+    for (int j = 0; j < KPL; ++j) {
+      const int i = base + lane + 64 * j;
+      key[j] = i < hi ? key_at(i) : 0u;
     }
-    // exclusive prefixes of (gt, eq) in thread order; a round counts at most
-    // KPT * NT = 4096 keys, so each fits 16 bits
-    int tot;
-    const int pre = block_scan<NT>(gt | (eq << 16), sm.wsum, &tot);
-    int eq_before = run_eq + (pre >> 16);
-    int pos = run_sel + (pre & 0xFFFF) + min(max(kr - run_eq, 0), pre >> 16);
+    uint64_t bm[KPL];
+    int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      if (i0 + j < n) {
-        bool sel = key[j] > T;
-        if (key[j] == T) {
-          sel = eq_before < kr;
-          ++eq_before;
+    for (int j = 0; j < KPL; ++j) {
+      const bool in = base + lane + 64 * j < hi;
+      above += int(in && (key[j] >> 21) > d1);
+      bm[j] = __ballot(in && (key[j] >> 21) == d1);
+      cnt += int(__popcll(bm[j]));
+    }
+    match += cnt;
+    if (!whole_bin && cnt != 0) {
+      int slot = 0;
+      if (use_cand) {
+        if (lane == 0) slot = atomicAdd(&sm.ncand, cnt);
+        slot = __builtin_amdgcn_readfirstlane(slot);
+      }
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        if ((bm[j] >> lane) & 1ull) {
+          atomicAdd(&sm.hist2[(key[j] >> 10) & uint32_t(kBins - 1)], 1u);
+          if (use_cand) sm.cand[slot + lane_prefix(bm[j])] = (uint32_t(wave) << 21) | (key[j] & 0x1FFFFFu);
         }
-        if (sel) {
-          if (pos < k) out[pos] = i0 + j;
-          ++pos;
-        }
+        slot += int(__popcll(bm[j]));
       }
     }
-    const int tot_gt = tot & 0xFFFF, tot_eq = tot >> 16;
-    run_sel += tot_gt + min(max(kr - run_eq, 0), tot_eq);
-    run_eq += tot_eq;
+  }
+  above = wave_sum(above);
+  if (lane == 0) {
+    sm.wgt[wave] = whole_bin ? above + match : above;
+    sm.weq[wave] = 0;
+  }
+  __syncthreads();
+
+  // ---- phase 4: T, the k-th largest key, and the per-segment counts -----------------
+  uint32_t T;
+  if (whole_bin) {
+    // all keys of bin d1 are taken: T sits just below the bin (d1 >= 1 here, since
+    // a whole bottom bin would mean n == k), and no tie is taken
+    T = (d1 << 21) - 1u;
+    kr = 0;
+  } else {
+    select_digit<NT, kBins>(sm, sm.hist2, kr);
+    const uint32_t p2 = (d1 << 11) | uint32_t(sm.sel_digit);  // top 22 bits of T
+    kr -= sm.sel_above;
+    if (use_cand) {
+      const int nc = sm.ncand;
+      for (int i = tid; i < nc; i += NT) {
+        const uint32_t key = (d1 << 21) | (sm.cand[i] & 0x1FFFFFu);
+        if ((key >> 10) == p2) atomicAdd(&sm.hist[key & 1023u], 1u);
+      }
+    } else {
+      for (int base = lo; base < hi; base += kStep) {
+        uint32_t key[KPL];
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+          const int i = base + lane + 64 * j;
+          key[j] = i < hi ? key_at(i) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < KPL; ++j)
+          if (base + lane + 64 * j < hi && (key[j] >> 10) == p2) atomicAdd(&sm.hist[key[j] & 1023u], 1u);
+      }
+    }
+    __syncthreads();
+    select_digit<NT, 1024>(sm, sm.hist, kr);
+    T = (p2 << 10) | uint32_t(sm.sel_digit);
+    kr -= sm.sel_above;  // ties (keys equal to T) still to take, >= 1
+    if (use_cand) {
+      const int nc = sm.ncand;
+      for (int i = tid; i < nc; i += NT) {
+        const uint32_t c = sm.cand[i];
+        const uint32_t key = (d1 << 21) | (c & 0x1FFFFFu);
+        if (key > T)
+          atomicAdd(&sm.wgt[c >> 21], 1);
+        else if (key == T)
+          atomicAdd(&sm.weq[c >> 21], 1);
+      }
+    } else {
+      int gt = 0, eq = 0;
+      for (int base = lo; base < hi; base += kStep) {
+        uint32_t key[KPL];
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+          const int i = base + lane + 64 * j;
+          key[j] = i < hi ? key_at(i) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+          const bool in = base + lane + 64 * j < hi && (key[j] >> 21) == d1;
+          gt += int(in && key[j] > T);
+          eq += int(in && key[j] == T);
+        }
+      }
+      gt = wave_sum(gt);
+      eq = wave_sum(eq);
+      if (lane == 0) {
+        sm.wgt[wave] += gt;
+        sm.weq[wave] = eq;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- phase 5: ordered emission ------------------------------------------------------
+  int gt_before = 0, eq_before = 0;
+  for (int w = 0; w < wave; ++w) {
+    gt_before += sm.wgt[w];
+    eq_before += sm.weq[w];
+  }
+  int pos = gt_before + min(eq_before, kr);  // output slots taken by earlier segments
+  int eq_run = eq_before;                    // ties met before this point
+  for (int base = lo; base < hi; base += kStep) {
+    uint32_t key[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int i = base + lane + 64 * j;
+      key[j] = i < hi ? key_at(i) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int i = base + lane + 64 * j;
+      const bool in = i < hi;
+      const bool is_eq = in && key[j] == T;
+      const uint64_t beq = __ballot(is_eq);
+      const bool sel = in && (key[j] > T || (is_eq && eq_run + lane_prefix(beq) < kr));
+      const uint64_t bsel = __ballot(sel);
+      const int p = pos + lane_prefix(bsel);
+      if (sel && p < k) out[p] = i;
+      pos += int(__popcll(bsel));
+      eq_run += int(__popcll(beq));
+    }
   }
 }
 
@@ -140,8 +293,6 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
   __shared__ Smem<NT> sm;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
   const int row = blockIdx.x;
   const int start = a.row_start ? min(max(a.row_start[row], 0), a.width) : 0;
   const int end = min(max(a.row_end[row], 0), a.width);
@@ -155,12 +306,14 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
   }
   const float *lr = a.logits + int64_t(row) * a.logits_row_stride + start;
   const bool cached = n <= cache_cap;
-  auto key_at = [&](int i) -> uint32_t { return cached ? s_keys[i] : order_key(lr[i]); };
 
-  // ---- pass 1: read the row, cache it, histogram of the top 11 bits ------------------
+  // ---- phases 1 and 2 -------------------------------------------------------------------
   // kUnroll independent loads per thread are issued before any of them is used, so a
   // batch costs one memory round trip
-  for (int i = tid; i < kBins; i += NT) sm.hist[i] = 0u;
+  for (int i = tid; i < kBins; i += NT) {
+    sm.hist[i] = 0u;
+    sm.hist2[i] = 0u;
+  }
   if (tid == 0) sm.ncand = 0;
   __syncthreads();
   for (int base = 0; base < n; base += kUnroll * NT) {
@@ -181,63 +334,12 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
     }
   }
   __syncthreads();
-  select_digit<NT>(sm, kBins, k);
-  const uint32_t d1 = uint32_t(sm.sel_digit);
-  int kr = k - sm.sel_above;
-  const int c1 = int(sm.hist[d1]);
+  select_digit<NT, kBins>(sm, sm.hist, k);
 
-  uint32_t T;  // the k-th largest key
-  if (c1 == kr) {
-    // the whole bin is selected: any key of the bin works as the cut, with all its
-    // keys taken; use the bin's lowest key so "above T or tie" selects exactly it
-    T = d1 << 21;
-    kr = n;  // every key equal to T is taken (there are at most c1 of them)
-    __syncthreads();
-    // keys of bin d1 are >= T; "key > T" plus all ties == the whole bin
-  } else {
-    __syncthreads();
-    const bool use_cand = c1 <= kMaxCand;
-    if (use_cand) {
-      for (int i = tid; i < n; i += NT) {
-        const uint32_t key = key_at(i);
-        if ((key >> 21) == d1) sm.cand[atomicAdd(&sm.ncand, 1)] = key;
-      }
-    }
-    // digits 2 (bits 20..10) and 3 (bits 9..0)
-    uint32_t prefix = d1 << 21, pmask = 0xFFE00000u;
-#pragma unroll
-    for (int dg = 0; dg < 2; ++dg) {
-      const int shift = dg == 0 ? 10 : 0;
-      const int nb = dg == 0 ? 2048 : 1024;
-      for (int i = tid; i < kBins; i += NT) sm.hist[i] = 0u;
-      __syncthreads();
-      if (use_cand) {
-        const int nc = sm.ncand;
-        for (int i = tid; i < nc; i += NT) {
-          const uint32_t key = sm.cand[i];
-          if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> shift) & uint32_t(nb - 1)], 1u);
-        }
-      } else {
-        for (int i = tid; i < n; i += NT) {
-          const uint32_t key = key_at(i);
-          if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> shift) & uint32_t(nb - 1)], 1u);
-        }
-      }
-      __syncthreads();
-      select_digit<NT>(sm, nb, kr);
-      prefix |= uint32_t(sm.sel_digit) << shift;
-      pmask |= uint32_t(nb - 1) << shift;
-      kr -= sm.sel_above;
-      __syncthreads();
-    }
-    T = prefix;
-  }
-
-  // ---- ordered emission ---------------------------------------------------------------
   if (cached)
-    emit<NT, 4096 / NT>(sm, [&](int i) { return s_keys[i]; }, n, k, T, kr, out);
+    finish_row<NT, 4>(sm, [&](int i) { return s_keys[i]; }, n, k, out);
   else
-    emit<NT, 4>(sm, [&](int i) { return order_key(lr[i]); }, n, k, T, kr, out);
+    finish_row<NT, 16>(sm, [&](int i) { return order_key(lr[i]); }, n, k, out);
 }
 
 }  // namespace
