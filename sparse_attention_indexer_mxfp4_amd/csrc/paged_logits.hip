@@ -21,8 +21,11 @@
 //   - holds its sequence's queries as MFMA A operands (16 heads x 128 channels per
 //     tile), reloading them when its share crosses into the next sequence.
 // K bytes go straight into MFMA B operands:
-//   fp8   lane L loads key L%16's bytes [16g, 16g+16) and [64+16g, 64+16g+16),
-//         g = L/16, from the block-flat page (the query uses the same byte order);
+//   fp8   lane L loads 16 bytes of key 8j + L/8 at byte 16 (L%8) for j = 0..7, so a
+//         wavefront load covers 8 whole key rows of the block-flat page; the wave
+//         stages them in its own LDS tile and reads back the MFMA B operands (lane L:
+//         key L%16 of the group, bytes [16g, 16g+16) and [64+16g, 64+16g+16),
+//         g = L/16, the query using the same byte order);
 //   MXFP4 lane L loads 16 bytes at run base + 16L - the run stores [chunk, key,
 //         byte], so one wavefront load covers the run's kilobyte exactly and lands
 //         in the scaled MFMA's operand order - plus the e8m0 byte at
@@ -44,6 +47,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunk = 64;
 constexpr int kMinChunksPerWave = 4;
+constexpr int kTileStride = 144;  // LDS bytes per key row of a wave's fp8 tile (128 + 16 against bank conflicts)
 
 // Exclusive prefix sum of per-thread values over the workgroup; returns the
 // thread's offset and stores the total in *total.
@@ -87,17 +91,28 @@ __device__ __forceinline__ void row_ends(const PagedArgs &a, int b, int cap, int
   }
 }
 
+// One 64-key chunk in registers. fp8: raw[j] holds bytes [16 (l % 8), +16) of key
+// 8 j + l / 8 (lane l): whole 128-byte key rows, so each wavefront load reads one
+// kilobyte of consecutive memory; the MFMA operands are formed through this wave's
+// LDS tile at scoring time. MXFP4: kb[kg] is already the B operand of key group kg.
 template <int FMT>
-struct Chunk {
+struct Chunk;
+template <>
+struct Chunk<0> {
+  v4i raw[8];
+  float ksc;
+};
+template <>
+struct Chunk<1> {
   v8i kb[4];
   int ksb[4];
-  float ksc;
 };
 
 template <int FMT, int HT, int NR>
 __global__ __launch_bounds__(kThreads) void paged_logits_kernel(PagedArgs a) {
   extern __shared__ int s_lds[];  // pref[B + 1], len[B]
   __shared__ int s_scan[kThreads / 64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_tile[FMT == 0 ? kThreads / 64 : 1][FMT == 0 ? kChunk * kTileStride : 16];
   int *s_pref = s_lds;
   int *s_len = s_lds + a.B + 1;
 
@@ -200,19 +215,25 @@ __global__ __launch_bounds__(kThreads) void paged_logits_kernel(PagedArgs a) {
   auto issue = [&](Chunk<FMT> &ch, int pg, int slot, int b, int c) {
     const int key0 = c * kChunk;
     const int len = s_len[b];
-    ch.ksc = 0.f;
+    if constexpr (FMT == 0) ch.ksc = 0.f;
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg) {
       const int s = key0 + kg * 16;  // 16 | P keeps a group inside one page
-      ch.kb[kg] = zero8();
-      ch.ksb[kg] = 127;
+      if constexpr (FMT == 0) {
+        ch.raw[2 * kg] = v4i{0, 0, 0, 0};
+        ch.raw[2 * kg + 1] = v4i{0, 0, 0, 0};
+      } else {
+        ch.kb[kg] = zero8();
+        ch.ksb[kg] = 127;
+      }
       if (s < len) {
         const int page = __builtin_amdgcn_readlane(pg, 4 * slot + kg);
         const uint8_t *pb = a.base + int64_t(page) * a.page_stride;
         const int e0 = a.page_shift >= 0 ? s & (P - 1) : s % P;
-        if (FMT == 0) {
-          const uint8_t *p = pb + (e0 + n) * 128 + g * 16;
-          ch.kb[kg] = cat(load16(p), load16(p + 64));
+        if constexpr (FMT == 0) {
+          const uint8_t *p = pb + (e0 + (lane >> 3)) * 128 + (lane & 7) * 16;
+          ch.raw[2 * kg] = load16(p);
+          ch.raw[2 * kg + 1] = load16(p + 8 * 128);
           if (g == kg) ch.ksc = *reinterpret_cast<const float *>(pb + P * 128 + 4 * (e0 + n));
         } else {
           const int run_i = e0 >> 4;
@@ -262,27 +283,48 @@ __global__ __launch_bounds__(kThreads) void paged_logits_kernel(PagedArgs a) {
 
   auto score = [&](const Chunk<FMT> &ch, int b, int c) {
     const int col = c * kChunk + lane;
-    float res[NR];
+    if constexpr (FMT == 0) {
+      // raw key rows into this wave's LDS tile; each key group's MFMA B operand is read
+      // back just before its MFMAs (lane (g, n) of group kg: bytes [16g, 16g+16) and
+      // [64+16g, 64+16g+16) of key 16 kg + n), so one operand is live at a time
 #pragma unroll
-    for (int j = 0; j < NR; ++j) {
-      float part[4];
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<v4i *>(&s_tile[wave][(8 * j + (lane >> 3)) * kTileStride + (lane & 7) * 16]) = ch.raw[j];
+    }
+    float part[NR][4];
 #pragma unroll
-      for (int kg = 0; kg < 4; ++kg) {
+    for (int kg = 0; kg < 4; ++kg) {
+      v8i kb;
+      if constexpr (FMT == 0) {
+        const uint8_t *t = &s_tile[wave][(kg * 16 + n) * kTileStride + g * 16];
+        kb = cat(*reinterpret_cast<const v4i *>(t), *reinterpret_cast<const v4i *>(t + 64));
+      } else {
+        kb = ch.kb[kg];
+      }
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
         float acc = 0.f;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
-          const v4f sc = FMT == 0 ? mfma_fp8(qa[j][ht], ch.kb[kg]) : mfma_fp4(qa[j][ht], ch.kb[kg], qs[j][ht], ch.ksb[kg]);
+          v4f sc;
+          if constexpr (FMT == 0)
+            sc = mfma_fp8(qa[j][ht], kb);
+          else
+            sc = mfma_fp4(qa[j][ht], kb, qs[j][ht], ch.ksb[kg]);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) acc = fmaf(wv[j][ht][jj], relu(sc[jj]), acc);
         }
-        part[kg] = acc;
+        part[j][kg] = acc;
       }
-      res[j] = transpose_reduce4(part);
     }
+    float res[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) res[j] = transpose_reduce4(part[j]);
     if (col < a.width) {
 #pragma unroll
       for (int j = 0; j < NR; ++j) {
-        const float val = FMT == 0 ? res[j] * ch.ksc : res[j];
+        float val = res[j];
+        if constexpr (FMT == 0) val *= ch.ksc;
         a.logits[(int64_t(b) * NR + j) * a.logits_row_stride + col] = col < end[j] ? val : ninf;
       }
     }

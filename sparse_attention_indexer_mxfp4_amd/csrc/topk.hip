@@ -18,8 +18,9 @@
 //      equal to T is counted against its wave;
 //   5. every wave then knows how many selected keys precede its segment and walks it
 //      once more, placing the selected keys with ballots and lane-prefix counts.
-// If the selected bin holds more keys than the candidate list (heavy ties), digit 3
-// and the per-wave counts come from extra passes over the row instead.
+// Rows too long for the key cache use the cache's LDS as their candidate list. If the
+// selected bin holds more keys than the list (heavy ties), digit 3 and the per-wave
+// counts come from extra passes over the row instead.
 #include "device.h"
 #include "launch.h"
 
@@ -127,11 +128,13 @@ __device__ __forceinline__ void segment(int n, int wave, int &lo, int &hi) {
 }
 
 // Phases 3 to 5 for one row, with the keys read through key_at (LDS or global) and
-// KPL keys per lane in flight per step.
+// KPL keys per lane in flight per step. The candidate list `cand` holds up to
+// cand_cap entries: the small list in Smem for rows whose keys sit in LDS, the unused
+// key cache for longer rows.
 template <int NT, int KPL, typename KeyAt>
-__device__ void finish_row(Smem<NT> &sm, KeyAt key_at, int n, int k, int32_t *out) {
+__device__ void finish_row(Smem<NT> &sm, KeyAt key_at, int n, int k, int32_t *out, uint32_t *cand,
+                           int cand_cap) {
   constexpr int kStep = 64 * KPL;
-  constexpr int kCand = Cfg<NT>::kCand;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int lo, hi;
   segment<NT, KPL>(n, wave, lo, hi);
@@ -140,7 +143,7 @@ __device__ void finish_row(Smem<NT> &sm, KeyAt key_at, int n, int k, int32_t *ou
   int kr = k - sm.sel_above;  // keys still needed from bin d1
   const int c1 = int(sm.hist[d1]);
   const bool whole_bin = c1 == kr;
-  const bool use_cand = !whole_bin && c1 <= kCand;
+  const bool use_cand = !whole_bin && c1 <= cand_cap;
   __syncthreads();  // every thread has read hist before it is cleared below
 
   // ---- phase 3: per-segment counts, candidates, digit-2 histogram --------------------
@@ -173,7 +176,7 @@ __device__ void finish_row(Smem<NT> &sm, KeyAt key_at, int n, int k, int32_t *ou
       for (int j = 0; j < KPL; ++j) {
         if ((bm[j] >> lane) & 1ull) {
           atomicAdd(&sm.hist2[(key[j] >> 10) & uint32_t(kBins - 1)], 1u);
-          if (use_cand) sm.cand[slot + lane_prefix(bm[j])] = (uint32_t(wave) << 21) | (key[j] & 0x1FFFFFu);
+          if (use_cand) cand[slot + lane_prefix(bm[j])] = (uint32_t(wave) << 21) | (key[j] & 0x1FFFFFu);
         }
         slot += int(__popcll(bm[j]));
       }
@@ -200,7 +203,7 @@ __device__ void finish_row(Smem<NT> &sm, KeyAt key_at, int n, int k, int32_t *ou
     if (use_cand) {
       const int nc = sm.ncand;
       for (int i = tid; i < nc; i += NT) {
-        const uint32_t key = (d1 << 21) | (sm.cand[i] & 0x1FFFFFu);
+        const uint32_t key = (d1 << 21) | (cand[i] & 0x1FFFFFu);
         if ((key >> 10) == p2) atomicAdd(&sm.hist[key & 1023u], 1u);
       }
     } else {
@@ -223,7 +226,7 @@ __device__ void finish_row(Smem<NT> &sm, KeyAt key_at, int n, int k, int32_t *ou
     if (use_cand) {
       const int nc = sm.ncand;
       for (int i = tid; i < nc; i += NT) {
-        const uint32_t c = sm.cand[i];
+        const uint32_t c = cand[i];
         const uint32_t key = (d1 << 21) | (c & 0x1FFFFFu);
         if (key > T)
           atomicAdd(&sm.wgt[c >> 21], 1);
@@ -273,16 +276,22 @@ __device__ void finish_row(Smem<NT> &sm, KeyAt key_at, int n, int k, int32_t *ou
     }
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
+      // most steps hold no tie and few selected keys: wave-uniform branches skip the
+      // lane-prefix work for them
       const int i = base + lane + 64 * j;
       const bool in = i < hi;
-      const bool is_eq = in && key[j] == T;
-      const uint64_t beq = __ballot(is_eq);
-      const bool sel = in && (key[j] > T || (is_eq && eq_run + lane_prefix(beq) < kr));
+      bool sel = in && key[j] > T;
+      const uint64_t beq = __ballot(in && key[j] == T);
+      if (beq != 0ull) {
+        sel = sel || ((beq >> lane) & 1ull && eq_run + lane_prefix(beq) < kr);
+        eq_run += int(__popcll(beq));
+      }
       const uint64_t bsel = __ballot(sel);
-      const int p = pos + lane_prefix(bsel);
-      if (sel && p < k) out[p] = i;
-      pos += int(__popcll(bsel));
-      eq_run += int(__popcll(beq));
+      if (bsel != 0ull) {
+        const int p = pos + lane_prefix(bsel);
+        if (sel && p < k) out[p] = i;
+        pos += int(__popcll(bsel));
+      }
     }
   }
 }
@@ -337,9 +346,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
   select_digit<NT, kBins>(sm, sm.hist, k);
 
   if (cached)
-    finish_row<NT, 4>(sm, [&](int i) { return s_keys[i]; }, n, k, out);
+    finish_row<NT, 4>(sm, [&](int i) { return s_keys[i]; }, n, k, out, sm.cand, Cfg<NT>::kCand);
   else
-    finish_row<NT, 16>(sm, [&](int i) { return order_key(lr[i]); }, n, k, out);
+    finish_row<NT, 16>(sm, [&](int i) { return order_key(lr[i]); }, n, k, out, s_keys, cache_cap);
 }
 
 }  // namespace
