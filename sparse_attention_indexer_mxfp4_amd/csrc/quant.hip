@@ -1,7 +1,12 @@
 // Quantisers that feed the indexer: the K store (quantise a key row and write it into
 // its cache slot) and the query quantiser. Page "vllm.models.deepseek_v41.amd.rocm",
 // rocm_mxfp4_indexer_k_store and rocm_mxfp4_indexer_q_quant (their quantise-and-write
-// part). One wavefront per 128-value row; lane L holds elements 2L and 2L+1.
+// part).
+//
+// K store: sixteen lanes per 128-value key (four keys per wavefront), lane l of a key
+// holding elements 8l .. 8l+7 from two 16-byte loads; maxima reduce over the 16 lanes
+// (fp8) or over 4 lanes (an MXFP4 block of 32) with DPP moves. The query quantiser
+// keeps one wavefront per 128-value row, lane L holding elements 2L and 2L+1.
 //
 //   fp8 K   scale = amax / 448 (IEEE fp32 division; 1.0 for an all-zero row), value
 //           e4m3(k / scale) rounded to nearest even and saturated; written into the
@@ -45,34 +50,97 @@ __device__ __forceinline__ float group16_max(float x) {
   return x;
 }
 
+constexpr int kKeysPerWG = 16;  // sixteen lanes per key
+
+// max over the 16 lanes of a DPP row (every lane receives it)
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));  // row_ror:8
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)));  // row_ror:4
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false)));  // row_ror:2
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false)));  // row_ror:1
+  return x;
+}
+
+// max over the 4 lanes of a quad (every lane receives it)
+__device__ __forceinline__ float quad_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));  // quad_perm [2,3,0,1]
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));  // quad_perm [1,0,3,2]
+  return x;
+}
+
 __global__ __launch_bounds__(256) void k_store_kernel(KStoreArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int i = blockIdx.x * kRowsPerWG + (threadIdx.x >> 6);
-  if (i >= a.N) return;
-  const int64_t slot = a.slots[i];
-  if (slot < 0) return;
-  const int64_t page = slot / a.page_size;
-  if (page >= a.num_pages) return;  // outside the pool: skipped like padding
-  const int e = int(slot % a.page_size);
-  uint8_t *pb = a.base + page * a.page_stride;
-  float x0, x1;
-  load_pair(a.k, a.k_dtype, int64_t(i) * a.k_row_stride + 2 * lane, x0, x1);
+  const int l = threadIdx.x & 15;  // lane within the key: elements 8l .. 8l+7
+  const int i = blockIdx.x * kKeysPerWG + (threadIdx.x >> 4);
+  // every lane of a 16-lane row takes part in the DPP reductions, so no lane leaves
+  // before them; rows without a valid key only skip the loads and stores
+  bool valid = i < a.N;
+  int64_t slot = valid ? a.slots[i] : -1;
+  int64_t page = slot >= 0 ? slot / a.page_size : -1;
+  valid = valid && slot >= 0 && page < a.num_pages;  // outside the pool: skipped like padding
+  float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // 16-byte loads when the rows allow them (wave-uniform), element loads otherwise
+  const int esize = a.k_dtype == 0 ? 4 : 2;
+  const bool vec = (reinterpret_cast<uintptr_t>(a.k) & 15) == 0 && (a.k_row_stride * esize) % 16 == 0;
+  if (valid) {
+    const int64_t e0 = int64_t(i) * a.k_row_stride + 8 * l;
+    if (a.k_dtype == 0) {
+      const float *p = static_cast<const float *>(a.k) + e0;
+      if (vec) {
+        const v4f lo = *reinterpret_cast<const v4f *>(p), hi = *reinterpret_cast<const v4f *>(p + 4);
+        x[0] = lo[0]; x[1] = lo[1]; x[2] = lo[2]; x[3] = lo[3];
+        x[4] = hi[0]; x[5] = hi[1]; x[6] = hi[2]; x[7] = hi[3];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = p[j];
+      }
+    } else {
+      const uint16_t *p = static_cast<const uint16_t *>(a.k) + e0;
+      if (vec) {
+        const v4i r = *reinterpret_cast<const v4i *>(p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[2 * j] = __uint_as_float(uint32_t(r[j]) << 16);
+          x[2 * j + 1] = __uint_as_float(uint32_t(r[j]) & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = bf16_to_f32(p[j]);
+      }
+    }
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
+  const int e = valid ? int(slot % a.page_size) : 0;
+  uint8_t *pb = a.base + (valid ? page : 0) * a.page_stride;
 
   if (a.fmt == 0) {
-    const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+    const float amax = row16_max(m);
     const float scale = amax == 0.f ? 1.f : __fdiv_rn(amax, 448.0f);
-    const uint32_t c0 = enc_e4m3(__fdiv_rn(x0, scale));
-    const uint32_t c1 = enc_e4m3(__fdiv_rn(x1, scale));
-    *reinterpret_cast<uint16_t *>(pb + e * 128 + 2 * lane) = uint16_t(c0 | (c1 << 8));
-    if (lane == 0) *reinterpret_cast<float *>(pb + a.page_size * 128 + 4 * e) = scale;
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w0 |= enc_e4m3(__fdiv_rn(x[j], scale)) << (8 * j);
+      w1 |= enc_e4m3(__fdiv_rn(x[4 + j], scale)) << (8 * j);
+    }
+    if (valid) {
+      *reinterpret_cast<uint2 *>(pb + e * 128 + 8 * l) = make_uint2(w0, w1);
+      if (l == 0) *reinterpret_cast<float *>(pb + a.page_size * 128 + 4 * e) = scale;
+    }
   } else {
-    const float amax = group16_max(fmaxf(fabsf(x0), fabsf(x1)));
+    // block b = l / 4 covers elements 32b .. 32b+31
+    const float amax = quad_max(m);
     const int bits = e8m0_bits(amax);
-    const float s = e8m0_inv_scale(bits);
-    const uint32_t byte = enc_e2m1(x0 * s) | (enc_e2m1(x1 * s) << 4);
-    const int run = e >> 4, u = e & 15;
-    pb[run * 1024 + (lane >> 4) * 256 + u * 16 + (lane & 15)] = uint8_t(byte);
-    if ((lane & 15) == 0) pb[a.page_size * 64 + run * 64 + (lane >> 4) * 16 + u] = uint8_t(bits);
+    const float sc = e8m0_inv_scale(bits);
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w |= (enc_e2m1(x[2 * j] * sc) | (enc_e2m1(x[2 * j + 1] * sc) << 4)) << (8 * j);
+    if (valid) {
+      // packed bytes 4l .. 4l+3 of the entry: chunk l/4, bytes 4(l%4) .. +3 of it
+      const int run = e >> 4, u = e & 15;
+      *reinterpret_cast<uint32_t *>(pb + run * 1024 + (l >> 2) * 256 + u * 16 + 4 * (l & 3)) = w;
+      if ((l & 3) == 0) pb[a.page_size * 64 + run * 64 + (l >> 2) * 16 + u] = uint8_t(bits);
+    }
   }
 }
 
@@ -99,7 +167,7 @@ __global__ __launch_bounds__(256) void q_quant_kernel(QQuantArgs a) {
 }  // namespace
 
 hipError_t launch_k_store(const KStoreArgs &a, hipStream_t stream) {
-  const int grid = (a.N + kRowsPerWG - 1) / kRowsPerWG;
+  const int grid = (a.N + kKeysPerWG - 1) / kKeysPerWG;
   k_store_kernel<<<grid, 256, 0, stream>>>(a);
   return hipGetLastError();
 }

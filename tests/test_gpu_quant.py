@@ -84,6 +84,32 @@ def test_k_store_bitexact(fmt, dtype, page_size, stride_pad):
     np.testing.assert_array_equal(pool.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("dtype,row_pad", [(torch.float32, 2), (torch.bfloat16, 3), (torch.float32, 4)])
+def test_k_store_row_strides(fmt, dtype, row_pad):
+    # key rows [N, 128] inside a wider buffer: padded rows, some not 16-byte aligned
+    rng = np.random.default_rng(103)
+    N, D, P = 77, 128, 16
+    num_pages = -(-N // P) + 1
+    big = rng.standard_normal((N, D + row_pad)).astype(np.float32)
+    kt = torch.from_numpy(big).to(dtype).to(DEV)[:, 1:D + 1]  # offset by one element as well
+    assert kt.stride(0) == D + row_pad
+    k32 = kt.float().cpu().numpy()
+    slots = rng.permutation(num_pages * P)[:N].astype(np.int64)
+    pb = (cache.fp8_page_bytes if fmt == "fp8" else cache.mxfp4_page_bytes)(P, D)
+    pool0 = np.zeros((num_pages, pb), dtype=np.uint8)
+    want = pool0.copy()
+    if fmt == "fp8":
+        codes, sc = formats.quantize_k_fp8(k32)
+        cache.store_fp8(want, slots, codes, sc, P)
+    else:
+        packed, sb = formats.quantize_mxfp4(k32)
+        cache.store_mxfp4(want, slots, packed, sb, P)
+    pool = torch.from_numpy(pool0).to(DEV)
+    ops.idx_k_store(pool, ops.FP8 if fmt == "fp8" else ops.MXFP4, P, kt, torch.from_numpy(slots).to(DEV))
+    np.testing.assert_array_equal(pool.cpu().numpy(), want)
+
+
 def test_k_store_empty_is_noop():
     pool = torch.zeros((2, 8448), dtype=torch.uint8, device=DEV)
     ops.idx_k_store(pool, ops.FP8, 64, torch.zeros((0, 128), device=DEV), torch.zeros(0, dtype=torch.int64, device=DEV))
