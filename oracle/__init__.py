@@ -13,7 +13,9 @@ the method fixes another precision:
 * ``cache``   - the byte layout of a paged K cache entry (fp8 block-flat pages and the
   MXFP4 run layout), as a writer and a reader;
 * ``indexer`` - the logits I[t, s] = sum_h w[t, h] * ReLU(q[t, h, :] . k[s, :]) with each
-  row's validity mask, the row ends of a paged decode / MTP step, and per-row top-k.
+  row's validity mask, the row ends of a paged decode / MTP step, and per-row top-k;
+* ``producers`` - what feeds the path: RMSNorm and RoPE of the keys before the store,
+  RoPE of the queries and the scaling of the weights.
 
 Sources are the vLLM API pages ``vllm.v1.attention.ops.rocm_aiter_mla_sparse``,
 ``vllm.models.deepseek_v41.amd.rocm``, ``vllm.v1.attention.backends.mla.rocm_aiter_mla``
@@ -21,4 +23,4 @@ and ``vllm.v1.attention.ops.rocm_paged_mxfp4_indexer``; each function names the
 section it follows.
 """
 
-from . import cache, formats, indexer  # noqa: F401
+from . import cache, formats, indexer, producers  # noqa: F401
