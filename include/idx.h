@@ -221,6 +221,54 @@ idx_status idx_k_store(const idx_paged_cache *cache, const void *k, int32_t k_dt
 idx_status idx_q_quant(const void *q, int32_t q_dtype, int64_t q_row_stride, int32_t T, int32_t H, int32_t D,
                        int32_t fmt, void *q_out, int32_t *q_scale_out, hipStream_t stream);
 
+/*
+ * idx_k_norm_rope_store - the key side of a step in one pass: RMSNorm, RoPE, then
+ * the K store. Page "vllm.models.deepseek_v41.amd.rocm", rocm_mxfp4_indexer_k_store
+ * (the pre-norm key, its position, the rotary cos/sin table, the norm weight and
+ * epsilon, the cache and the slot mapping go to one cache op).
+ *
+ *   k, k_dtype, k_row_stride, slot_mapping, N   as idx_k_store (pre-norm keys).
+ *   norm_weight   [D] fp32, 16-byte aligned; eps > 0.
+ *   positions     [N] int64: the rotary position of key i, clamped to
+ *                 [0, max_position - 1] (a compressed cache passes the position
+ *                 of the stored key).
+ *   cos_sin       [max_position, rope_dim] fp32: row p holds cos of the rope_dim/2
+ *                 pair angles at position p, then their sin.
+ *   rope_dim      even, 0..D (0: no rotation; positions and cos_sin may be NULL).
+ *   Each key becomes y = x / sqrt(mean(x^2) + eps) * norm_weight (fp32, correctly
+ *   rounded square root and division); the trailing rope_dim channels of y are
+ *   rotated in pairs (D - rope_dim + 2i, D - rope_dim + 2i + 1) by
+ *   (a, b) -> (a cos_i - b sin_i, b cos_i + a sin_i), the GPT-J form whose inverse
+ *   page "vllm.v1.attention.ops.rocm_aiter_mla_sparse" gives (_inverse_rope_gptj_kernel);
+ *   the result is quantised and written exactly as idx_k_store does.
+ *   Limits: D == 128, N >= 0.
+ */
+idx_status idx_k_norm_rope_store(const idx_paged_cache *cache, const void *k, int32_t k_dtype, int64_t k_row_stride,
+                                 const int64_t *positions, const float *cos_sin, int32_t max_position,
+                                 int32_t rope_dim, const float *norm_weight, float eps,
+                                 const int64_t *slot_mapping, int32_t N, hipStream_t stream);
+
+/*
+ * idx_q_rope_quant - the query side of a step in one pass: RoPE, quantisation and
+ * the weights scaled for scoring. Page "vllm.models.deepseek_v41.amd.rocm",
+ * rocm_mxfp4_indexer_q_quant (queries, positions, the rotary table and the indexer
+ * weights in; quantised queries and weights times softmax_scale * n_head^-0.5 out).
+ *
+ *   q, q_dtype, q_row_stride, T, H, D, fmt, q_out, q_scale_out   as idx_q_quant,
+ *                 the quantisation applying to the rotated query.
+ *   positions     [T] int64: token t's rotary position (all heads), clamped as in
+ *                 idx_k_norm_rope_store; cos_sin, max_position, rope_dim likewise.
+ *   weights       [T, H] fp32, row t at weights + t*weights_row_stride (>= H).
+ *   weight_scale  multiplies every weight (softmax_scale * n_head^-0.5 on the page).
+ *   weights_out   [T, H] fp32 dense: weights * weight_scale, one fp32 rounding.
+ *   Limits: D == 128, T, H >= 0; q_out 8-byte (fp8) or 4-byte (MXFP4) aligned.
+ */
+idx_status idx_q_rope_quant(const void *q, int32_t q_dtype, int64_t q_row_stride, const int64_t *positions,
+                            const float *cos_sin, int32_t max_position, int32_t rope_dim, const float *weights,
+                            int64_t weights_row_stride, float weight_scale, int32_t T, int32_t H, int32_t D,
+                            int32_t fmt, void *q_out, int32_t *q_scale_out, float *weights_out,
+                            hipStream_t stream);
+
 /* Static text naming a status; never NULL. */
 const char *idx_status_str(idx_status s);
 /* IDX_ABI_VERSION of the built library. */

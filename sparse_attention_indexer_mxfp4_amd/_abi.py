@@ -23,7 +23,8 @@ STATUS_NAMES = {
 # every function include/idx.h declares
 EXPORTS = (
     "idx_page_bytes", "idx_mqa_logits", "idx_paged_mqa_logits", "idx_paged_mqa_logits_workspace", "idx_topk",
-    "idx_topk_workspace", "idx_k_store", "idx_q_quant", "idx_status_str", "idx_abi_version",
+    "idx_topk_workspace", "idx_k_store", "idx_q_quant", "idx_k_norm_rope_store", "idx_q_rope_quant",
+    "idx_status_str", "idx_abi_version",
 )
 
 
@@ -52,6 +53,7 @@ _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
+_F32 = ctypes.c_float
 
 
 def _declare(lib: ctypes.CDLL) -> None:
@@ -66,6 +68,9 @@ def _declare(lib: ctypes.CDLL) -> None:
         "idx_topk_workspace": (_SZ, [_I32, _I32, _I32]),
         "idx_k_store": (_I32, [cache_p, _P, _I32, _I64, _P, _I32, _P]),
         "idx_q_quant": (_I32, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _P, _P, _P]),
+        "idx_k_norm_rope_store": (_I32, [cache_p, _P, _I32, _I64, _P, _P, _I32, _I32, _P, _F32, _P, _I32, _P]),
+        "idx_q_rope_quant": (_I32, [_P, _I32, _I64, _P, _P, _I32, _I32, _P, _I64, _F32, _I32, _I32, _I32, _I32, _P,
+                                    _P, _P, _P]),
         "idx_status_str": (ctypes.c_char_p, [_I32]),
         "idx_abi_version": (_I32, []),
     }

@@ -114,7 +114,24 @@ idx_status idx_k_store(const idx_paged_cache *cache, const void *k, int32_t k_dt
   int cus = 0;
   if ((s = current_device(&cus)) != IDX_OK) return s;
   idx::KStoreArgs a{static_cast<uint8_t *>(cache->base), cache->page_stride_bytes, cache->page_size,
-                    cache->num_pages, cache->fmt, k, k_dtype, k_row_stride, slot_mapping, N};
+                    cache->num_pages, cache->fmt, k, k_dtype, k_row_stride, slot_mapping, N,
+                    nullptr, 0.f, nullptr, nullptr, 0, 0};
+  return launched(idx::launch_k_store(a, stream));
+}
+
+idx_status idx_k_norm_rope_store(const idx_paged_cache *cache, const void *k, int32_t k_dtype, int64_t k_row_stride,
+                                 const int64_t *positions, const float *cos_sin, int32_t max_position,
+                                 int32_t rope_dim, const float *norm_weight, float eps,
+                                 const int64_t *slot_mapping, int32_t N, hipStream_t stream) {
+  bool empty = false;
+  idx_status s = idx::check_k_store(cache, k, k_dtype, k_row_stride, slot_mapping, N, &empty);
+  if (s != IDX_OK || empty) return s;
+  if ((s = idx::check_norm_rope(positions, cos_sin, max_position, rope_dim, norm_weight, eps)) != IDX_OK) return s;
+  int cus = 0;
+  if ((s = current_device(&cus)) != IDX_OK) return s;
+  idx::KStoreArgs a{static_cast<uint8_t *>(cache->base), cache->page_stride_bytes, cache->page_size,
+                    cache->num_pages, cache->fmt, k, k_dtype, k_row_stride, slot_mapping, N,
+                    norm_weight, eps, positions, cos_sin, max_position, rope_dim};
   return launched(idx::launch_k_store(a, stream));
 }
 
@@ -127,6 +144,24 @@ idx_status idx_q_quant(const void *q, int32_t q_dtype, int64_t q_row_stride, int
   if ((s = current_device(&cus)) != IDX_OK) return s;
   idx::QQuantArgs a{q, q_dtype, q_row_stride, T, H, fmt, static_cast<uint8_t *>(q_out), q_scale_out};
   return launched(idx::launch_q_quant(a, stream));
+}
+
+idx_status idx_q_rope_quant(const void *q, int32_t q_dtype, int64_t q_row_stride, const int64_t *positions,
+                            const float *cos_sin, int32_t max_position, int32_t rope_dim, const float *weights,
+                            int64_t weights_row_stride, float weight_scale, int32_t T, int32_t H, int32_t D,
+                            int32_t fmt, void *q_out, int32_t *q_scale_out, float *weights_out,
+                            hipStream_t stream) {
+  bool empty = false;
+  idx_status s = idx::check_q_rope_quant(q, q_dtype, q_row_stride, positions, cos_sin, max_position, rope_dim,
+                                         weights, weights_row_stride, T, H, D, fmt, q_out, q_scale_out, weights_out,
+                                         &empty);
+  if (s != IDX_OK || empty) return s;
+  int cus = 0;
+  if ((s = current_device(&cus)) != IDX_OK) return s;
+  idx::QRopeArgs a{q, q_dtype, q_row_stride, positions, cos_sin, max_position, rope_dim, weights,
+                   weights_row_stride, weight_scale, T, H, fmt, static_cast<uint8_t *>(q_out), q_scale_out,
+                   weights_out};
+  return launched(idx::launch_q_rope_quant(a, stream));
 }
 
 const char *idx_status_str(idx_status s) {

@@ -66,6 +66,29 @@ struct KStoreArgs {
   int64_t k_row_stride;  // elements
   const int64_t *slots;
   int32_t N;
+  // RMSNorm + RoPE before the store (norm_weight != NULL)
+  const float *norm_weight;
+  float eps;
+  const int64_t *positions;
+  const float *cos_sin;
+  int32_t max_position, rope_dim;
+};
+
+struct QRopeArgs {
+  const void *q;
+  int32_t q_dtype;
+  int64_t q_row_stride;  // elements
+  const int64_t *positions;
+  const float *cos_sin;
+  int32_t max_position, rope_dim;
+  const float *weights;
+  int64_t weights_row_stride;  // elements
+  float weight_scale;
+  int32_t T, H;
+  int32_t fmt;
+  uint8_t *q_out;
+  int32_t *q_scale_out;
+  float *weights_out;
 };
 
 struct QQuantArgs {
@@ -83,5 +106,6 @@ hipError_t launch_paged_logits(const PagedArgs &a, int num_cus, hipStream_t stre
 hipError_t launch_topk(const TopkArgs &a, int num_cus, hipStream_t stream);
 hipError_t launch_k_store(const KStoreArgs &a, hipStream_t stream);
 hipError_t launch_q_quant(const QQuantArgs &a, hipStream_t stream);
+hipError_t launch_q_rope_quant(const QRopeArgs &a, hipStream_t stream);
 
 }  // namespace idx

@@ -5,8 +5,12 @@
 //
 // K store: sixteen lanes per 128-value key (four keys per wavefront), lane l of a key
 // holding elements 8l .. 8l+7 from two 16-byte loads; maxima reduce over the 16 lanes
-// (fp8) or over 4 lanes (an MXFP4 block of 32) with DPP moves. The query quantiser
-// keeps one wavefront per 128-value row, lane L holding elements 2L and 2L+1.
+// (fp8) or over 4 lanes (an MXFP4 block of 32) with DPP moves. The fused variant
+// applies RMSNorm and GPT-J RoPE before quantising (rocm_mxfp4_indexer_k_store on the
+// same page hands the cache op the pre-norm key, its position, the rotary table and
+// the norm weight). The fused query op (rocm_mxfp4_indexer_q_quant) rotates, quantises
+// and scales the weights with the same lane layout. The plain query quantiser keeps
+// one wavefront per 128-value row, lane L holding elements 2L and 2L+1.
 //
 //   fp8 K   scale = amax / 448 (IEEE fp32 division; 1.0 for an all-zero row), value
 //           e4m3(k / scale) rounded to nearest even and saturated; written into the
@@ -61,6 +65,15 @@ __device__ __forceinline__ float row16_max(float x) {
   return x;
 }
 
+// sum over the 16 lanes of a DPP row (every lane receives it)
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror:8
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));  // row_ror:4
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));  // row_ror:2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));  // row_ror:1
+  return x;
+}
+
 // max over the 4 lanes of a quad (every lane receives it)
 __device__ __forceinline__ float quad_max(float x) {
   x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));  // quad_perm [2,3,0,1]
@@ -68,53 +81,83 @@ __device__ __forceinline__ float quad_max(float x) {
   return x;
 }
 
-__global__ __launch_bounds__(256) void k_store_kernel(KStoreArgs a) {
-  const int l = threadIdx.x & 15;  // lane within the key: elements 8l .. 8l+7
-  const int i = blockIdx.x * kKeysPerWG + (threadIdx.x >> 4);
-  // every lane of a 16-lane row takes part in the DPP reductions, so no lane leaves
-  // before them; rows without a valid key only skip the loads and stores
-  bool valid = i < a.N;
-  int64_t slot = valid ? a.slots[i] : -1;
-  int64_t page = slot >= 0 ? slot / a.page_size : -1;
-  valid = valid && slot >= 0 && page < a.num_pages;  // outside the pool: skipped like padding
-  float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  // 16-byte loads when the rows allow them (wave-uniform), element loads otherwise
-  const int esize = a.k_dtype == 0 ? 4 : 2;
-  const bool vec = (reinterpret_cast<uintptr_t>(a.k) & 15) == 0 && (a.k_row_stride * esize) % 16 == 0;
-  if (valid) {
-    const int64_t e0 = int64_t(i) * a.k_row_stride + 8 * l;
-    if (a.k_dtype == 0) {
-      const float *p = static_cast<const float *>(a.k) + e0;
-      if (vec) {
-        const v4f lo = *reinterpret_cast<const v4f *>(p), hi = *reinterpret_cast<const v4f *>(p + 4);
-        x[0] = lo[0]; x[1] = lo[1]; x[2] = lo[2]; x[3] = lo[3];
-        x[4] = hi[0]; x[5] = hi[1]; x[6] = hi[2]; x[7] = hi[3];
-      } else {
+// Elements 8l .. 8l+7 of a 128-value fp32 / bf16 row: 16-byte loads when `vec` (the
+// rows are 16-byte aligned), element loads otherwise.
+__device__ __forceinline__ void load_row8(const void *base, int dtype, int64_t e0, bool vec, float (&x)[8]) {
+  if (dtype == 0) {
+    const float *p = static_cast<const float *>(base) + e0;
+    if (vec) {
+      const v4f lo = *reinterpret_cast<const v4f *>(p), hi = *reinterpret_cast<const v4f *>(p + 4);
+      x[0] = lo[0]; x[1] = lo[1]; x[2] = lo[2]; x[3] = lo[3];
+      x[4] = hi[0]; x[5] = hi[1]; x[6] = hi[2]; x[7] = hi[3];
+    } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = p[j];
+      for (int j = 0; j < 8; ++j) x[j] = p[j];
+    }
+  } else {
+    const uint16_t *p = static_cast<const uint16_t *>(base) + e0;
+    if (vec) {
+      const v4i r = *reinterpret_cast<const v4i *>(p);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = __uint_as_float(uint32_t(r[j]) << 16);
+        x[2 * j + 1] = __uint_as_float(uint32_t(r[j]) & 0xFFFF0000u);
       }
     } else {
-      const uint16_t *p = static_cast<const uint16_t *>(a.k) + e0;
-      if (vec) {
-        const v4i r = *reinterpret_cast<const v4i *>(p);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          x[2 * j] = __uint_as_float(uint32_t(r[j]) << 16);
-          x[2 * j + 1] = __uint_as_float(uint32_t(r[j]) & 0xFFFF0000u);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = bf16_to_f32(p[j]);
-      }
+      for (int j = 0; j < 8; ++j) x[j] = bf16_to_f32(p[j]);
     }
   }
+}
+
+__device__ __forceinline__ bool rows_vec(const void *base, int dtype, int64_t row_stride) {
+  const int esize = dtype == 0 ? 4 : 2;
+  return (reinterpret_cast<uintptr_t>(base) & 15) == 0 && (row_stride * esize) % 16 == 0;
+}
+
+// RMSNorm over the 16 lanes of a row: x / sqrt(mean(x^2) + eps) * weight, in fp32
+// (the mean is the lane sum times 2^-7, exact; the reciprocal root is a correctly
+// rounded square root and division).
+__device__ __forceinline__ void rms_norm8(float (&x)[8], const float *weight, int l, float eps) {
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ss = fmaf(x[j], x[j], ss);
+  const float ms = row16_sum(ss) * 0.0078125f;
+  const float r = __fdiv_rn(1.0f, __fsqrt_rn(ms + eps));
+  const v4f w0 = *reinterpret_cast<const v4f *>(weight + 8 * l), w1 = *reinterpret_cast<const v4f *>(weight + 8 * l + 4);
+  x[0] = x[0] * r * w0[0]; x[1] = x[1] * r * w0[1]; x[2] = x[2] * r * w0[2]; x[3] = x[3] * r * w0[3];
+  x[4] = x[4] * r * w1[0]; x[5] = x[5] * r * w1[1]; x[6] = x[6] * r * w1[2]; x[7] = x[7] * r * w1[3];
+}
+
+// GPT-J RoPE of the trailing rope_dim channels: pair (d, d+1), d = 128 - rope_dim + 2i,
+// rotated by (cos_i, sin_i) of table row `pos` to (a cos - b sin, b cos + a sin).
+__device__ __forceinline__ void rope8(float (&x)[8], const float *cos_sin, int64_t pos, int rope_dim, int l) {
+  const int lo = 128 - rope_dim, half = rope_dim >> 1;
+  const float *row = cos_sin + pos * rope_dim;
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const int d = 8 * l + j;
+    if (d >= lo) {
+      const int i = (d - lo) >> 1;
+      const float c = row[i], s = row[half + i];
+      const float a = x[j], b = x[j + 1];
+      x[j] = a * c - b * s;
+      x[j + 1] = b * c + a * s;
+    }
+  }
+}
+
+__device__ __forceinline__ int64_t clamp_pos(int64_t p, int max_position) {
+  return p < 0 ? 0 : (p >= max_position ? int64_t(max_position - 1) : p);
+}
+
+// Quantise a key row held as 8 values per lane and write it into its cache entry.
+__device__ __forceinline__ void store_key(const float (&x)[8], int fmt, uint8_t *pb, int page_size, int e, int l,
+                                          bool valid) {
   float m = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
-  const int e = valid ? int(slot % a.page_size) : 0;
-  uint8_t *pb = a.base + (valid ? page : 0) * a.page_stride;
-
-  if (a.fmt == 0) {
+  if (fmt == 0) {
     const float amax = row16_max(m);
     const float scale = amax == 0.f ? 1.f : __fdiv_rn(amax, 448.0f);
     uint32_t w0 = 0, w1 = 0;
@@ -125,7 +168,7 @@ __global__ __launch_bounds__(256) void k_store_kernel(KStoreArgs a) {
     }
     if (valid) {
       *reinterpret_cast<uint2 *>(pb + e * 128 + 8 * l) = make_uint2(w0, w1);
-      if (l == 0) *reinterpret_cast<float *>(pb + a.page_size * 128 + 4 * e) = scale;
+      if (l == 0) *reinterpret_cast<float *>(pb + page_size * 128 + 4 * e) = scale;
     }
   } else {
     // block b = l / 4 covers elements 32b .. 32b+31
@@ -139,7 +182,69 @@ __global__ __launch_bounds__(256) void k_store_kernel(KStoreArgs a) {
       // packed bytes 4l .. 4l+3 of the entry: chunk l/4, bytes 4(l%4) .. +3 of it
       const int run = e >> 4, u = e & 15;
       *reinterpret_cast<uint32_t *>(pb + run * 1024 + (l >> 2) * 256 + u * 16 + 4 * (l & 3)) = w;
-      if ((l & 3) == 0) pb[a.page_size * 64 + run * 64 + (l >> 2) * 16 + u] = uint8_t(bits);
+      if ((l & 3) == 0) pb[page_size * 64 + run * 64 + (l >> 2) * 16 + u] = uint8_t(bits);
+    }
+  }
+}
+
+// K store, optionally preceded by RMSNorm and RoPE (NORM_ROPE). Every lane of a
+// 16-lane row takes part in the DPP reductions, so no lane leaves before them; rows
+// without a valid key only skip the loads and stores.
+template <bool NORM_ROPE>
+__global__ __launch_bounds__(256) void k_store_kernel(KStoreArgs a) {
+  const int l = threadIdx.x & 15;  // lane within the key: elements 8l .. 8l+7
+  const int i = blockIdx.x * kKeysPerWG + (threadIdx.x >> 4);
+  bool valid = i < a.N;
+  const int64_t slot = valid ? a.slots[i] : -1;
+  const int64_t page = slot >= 0 ? slot / a.page_size : -1;
+  valid = valid && slot >= 0 && page < a.num_pages;  // outside the pool: skipped like padding
+  float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (valid) load_row8(a.k, a.k_dtype, int64_t(i) * a.k_row_stride + 8 * l, rows_vec(a.k, a.k_dtype, a.k_row_stride), x);
+  if (NORM_ROPE) {
+    rms_norm8(x, a.norm_weight, l, a.eps);
+    if (valid && a.rope_dim > 0) rope8(x, a.cos_sin, clamp_pos(a.positions[i], a.max_position), a.rope_dim, l);
+  }
+  const int e = valid ? int(slot % a.page_size) : 0;
+  uint8_t *pb = a.base + (valid ? page : 0) * a.page_stride;
+  store_key(x, a.fmt, pb, a.page_size, e, l, valid);
+}
+
+// Query side of a step: RoPE, quantisation and the weight scale. Sixteen lanes per
+// (token, head) row of 128 values.
+__global__ __launch_bounds__(256) void q_rope_quant_kernel(QRopeArgs a) {
+  const int l = threadIdx.x & 15;
+  const int64_t row = int64_t(blockIdx.x) * kKeysPerWG + (threadIdx.x >> 4);  // t * H + h
+  const bool valid = row < int64_t(a.T) * a.H;
+  const int64_t t = valid ? row / a.H : 0;
+  const int h = valid ? int(row % a.H) : 0;
+  float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (valid) {
+    load_row8(a.q, a.q_dtype, t * a.q_row_stride + int64_t(h) * 128 + 8 * l, rows_vec(a.q, a.q_dtype, a.q_row_stride), x);
+    if (a.rope_dim > 0) rope8(x, a.cos_sin, clamp_pos(a.positions[t], a.max_position), a.rope_dim, l);
+    if (l == 0) a.weights_out[row] = a.weights[t * a.weights_row_stride + h] * a.weight_scale;
+  }
+  if (a.fmt == 0) {
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w0 |= enc_e4m3(x[j]) << (8 * j);
+      w1 |= enc_e4m3(x[4 + j]) << (8 * j);
+    }
+    if (valid) *reinterpret_cast<uint2 *>(a.q_out + row * 128 + 8 * l) = make_uint2(w0, w1);
+  } else {
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
+    const float amax = quad_max(m);
+    const int bits = e8m0_bits(amax);
+    const float sc = e8m0_inv_scale(bits);
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w |= (enc_e2m1(x[2 * j] * sc) | (enc_e2m1(x[2 * j + 1] * sc) << 4)) << (8 * j);
+    if (valid) {
+      *reinterpret_cast<uint32_t *>(a.q_out + row * 64 + 4 * l) = w;
+      // byte b of the head's int32 is block b's scale (little-endian)
+      if ((l & 3) == 0) reinterpret_cast<uint8_t *>(a.q_scale_out)[row * 4 + (l >> 2)] = uint8_t(bits);
     }
   }
 }
@@ -168,7 +273,17 @@ __global__ __launch_bounds__(256) void q_quant_kernel(QQuantArgs a) {
 
 hipError_t launch_k_store(const KStoreArgs &a, hipStream_t stream) {
   const int grid = (a.N + kKeysPerWG - 1) / kKeysPerWG;
-  k_store_kernel<<<grid, 256, 0, stream>>>(a);
+  if (a.norm_weight)
+    k_store_kernel<true><<<grid, 256, 0, stream>>>(a);
+  else
+    k_store_kernel<false><<<grid, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_q_rope_quant(const QRopeArgs &a, hipStream_t stream) {
+  const int64_t rows = int64_t(a.T) * a.H;
+  const int64_t grid = (rows + kKeysPerWG - 1) / kKeysPerWG;
+  q_rope_quant_kernel<<<dim3(unsigned(grid)), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -141,4 +141,32 @@ idx_status check_q_quant(const void *q, int32_t q_dtype, int64_t q_row_stride, i
   return IDX_OK;
 }
 
+idx_status check_norm_rope(const void *positions, const void *cos_sin, int32_t max_position, int32_t rope_dim,
+                           const void *norm_weight, float eps) {
+  if (rope_dim < 0 || rope_dim > kHeadDim || rope_dim % 2) return IDX_ERR_SHAPE;
+  if (rope_dim > 0) {
+    if (!positions || !cos_sin) return IDX_ERR_NULL;
+    if (max_position < 1) return IDX_ERR_SHAPE;
+    if (!aligned(positions, 8) || !aligned(cos_sin, 4)) return IDX_ERR_STRIDE;
+  }
+  if (norm_weight) {
+    if (!(eps > 0.f) || eps != eps) return IDX_ERR_SHAPE;
+    if (!aligned(norm_weight, 16)) return IDX_ERR_STRIDE;
+  }
+  return IDX_OK;
+}
+
+idx_status check_q_rope_quant(const void *q, int32_t q_dtype, int64_t q_row_stride, const void *positions,
+                              const void *cos_sin, int32_t max_position, int32_t rope_dim, const void *weights,
+                              int64_t weights_row_stride, int32_t T, int32_t H, int32_t D, int32_t fmt,
+                              const void *q_out, const void *q_scale_out, const void *weights_out, bool *empty) {
+  idx_status s = check_q_quant(q, q_dtype, q_row_stride, T, H, D, fmt, q_out, q_scale_out, empty);
+  if (s != IDX_OK || *empty) return s;
+  if ((s = check_norm_rope(positions, cos_sin, max_position, rope_dim, nullptr, 0.f)) != IDX_OK) return s;
+  if (!weights || !weights_out) return IDX_ERR_NULL;
+  if (weights_row_stride < H || !aligned(weights, 4) || !aligned(weights_out, 4)) return IDX_ERR_STRIDE;
+  if (!aligned(q_out, fmt == IDX_KV_FP8_E4M3 ? 8 : 4)) return IDX_ERR_STRIDE;
+  return IDX_OK;
+}
+
 }  // namespace idx

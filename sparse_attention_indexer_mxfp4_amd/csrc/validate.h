@@ -45,4 +45,14 @@ idx_status check_k_store(const idx_paged_cache *cache, const void *k, int32_t k_
 idx_status check_q_quant(const void *q, int32_t q_dtype, int64_t q_row_stride, int32_t T, int32_t H, int32_t D,
                          int32_t fmt, const void *q_out, const void *q_scale_out, bool *empty);
 
+// The RoPE table and RMSNorm arguments of the fused producers (norm_weight may be
+// NULL when no norm is applied, as in the query op).
+idx_status check_norm_rope(const void *positions, const void *cos_sin, int32_t max_position, int32_t rope_dim,
+                           const void *norm_weight, float eps);
+
+idx_status check_q_rope_quant(const void *q, int32_t q_dtype, int64_t q_row_stride, const void *positions,
+                              const void *cos_sin, int32_t max_position, int32_t rope_dim, const void *weights,
+                              int64_t weights_row_stride, int32_t T, int32_t H, int32_t D, int32_t fmt,
+                              const void *q_out, const void *q_scale_out, const void *weights_out, bool *empty);
+
 }  // namespace idx

@@ -161,3 +161,62 @@ def idx_q_quant(q: torch.Tensor, fmt: int):
         scale = torch.empty((T, H), dtype=torch.int32, device=q.device)
     _abi.check(_abi.lib().idx_q_quant(_ptr(q), dt, q.stride(0), T, H, D, fmt, _ptr(out), _ptr(scale), _stream()))
     return out, scale
+
+
+def _rope_args(positions: torch.Tensor | None, cos_sin: torch.Tensor | None, rope_dim: int):
+    if rope_dim == 0:
+        return None, None, 1
+    if positions is None or cos_sin is None:
+        raise ValueError("RoPE needs positions and a cos/sin table")
+    _need(positions, torch.int64, "positions"); _contig(positions, "positions")
+    _need(cos_sin, torch.float32, "cos_sin"); _contig(cos_sin, "cos_sin")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != rope_dim:
+        raise ValueError("cos_sin must be [max_position, rope_dim]")
+    return positions, cos_sin, cos_sin.shape[0]
+
+
+def idx_k_norm_rope_store(pool: torch.Tensor, fmt: int, page_size: int, k: torch.Tensor, slot_mapping: torch.Tensor,
+                          positions: torch.Tensor | None, cos_sin: torch.Tensor | None, rope_dim: int,
+                          norm_weight: torch.Tensor, eps: float) -> None:
+    """RMSNorm (norm_weight [128] f32, eps) and GPT-J RoPE of pre-norm keys k [N, 128]
+    (f32 or bf16), then the K store into their slots of the pool."""
+    cache = paged_cache(pool, fmt, page_size)
+    if k.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("k must be float32 or bfloat16")
+    _need(slot_mapping, torch.int64, "slot_mapping"); _contig(slot_mapping, "slot_mapping")
+    _need(norm_weight, torch.float32, "norm_weight"); _contig(norm_weight, "norm_weight")
+    if k.stride(1) != 1:
+        raise ValueError("k rows must be dense")
+    pos, cs, maxp = _rope_args(positions, cos_sin, rope_dim)
+    dt = IDX_IN_F32 if k.dtype == torch.float32 else IDX_IN_BF16
+    _abi.check(_abi.lib().idx_k_norm_rope_store(ctypes.byref(cache), _ptr(k), dt, k.stride(0), _ptr(pos), _ptr(cs),
+                                                maxp, rope_dim, _ptr(norm_weight), float(eps), _ptr(slot_mapping),
+                                                k.shape[0], _stream()))
+
+
+def idx_q_rope_quant(q: torch.Tensor, fmt: int, positions: torch.Tensor | None, cos_sin: torch.Tensor | None,
+                     rope_dim: int, weights: torch.Tensor, weight_scale: float):
+    """GPT-J RoPE of queries q [T, H, 128] (f32 or bf16), quantised as idx_q_quant, and
+    weights [T, H] f32 times weight_scale. Returns (q_out, q_scale or None, weights_out)."""
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("q must be float32 or bfloat16")
+    T, H, D = q.shape
+    if q.stride(2) != 1 or q.stride(1) != D:
+        raise ValueError("q heads must be dense")
+    _need(weights, torch.float32, "weights")
+    if weights.dim() != 2 or tuple(weights.shape) != (T, H) or weights.stride(1) != 1:
+        raise ValueError("weights must be [T, H] with dense rows")
+    pos, cs, maxp = _rope_args(positions, cos_sin, rope_dim)
+    dt = IDX_IN_F32 if q.dtype == torch.float32 else IDX_IN_BF16
+    if fmt == FP8:
+        out = torch.empty((T, H, D), dtype=torch.uint8, device=q.device)
+        scale = None
+    else:
+        out = torch.empty((T, H, D // 2), dtype=torch.uint8, device=q.device)
+        scale = torch.empty((T, H), dtype=torch.int32, device=q.device)
+    w_out = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _abi.check(_abi.lib().idx_q_rope_quant(_ptr(q), dt, q.stride(0), _ptr(pos), _ptr(cs), maxp, rope_dim,
+                                           _ptr(weights), weights.stride(0), float(weight_scale), T, H, D, fmt,
+                                           _ptr(out), _ptr(scale), _ptr(w_out), _stream()))
+    return out, scale, w_out
+

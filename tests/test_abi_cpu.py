@@ -166,6 +166,31 @@ def test_k_store_and_q_quant_checks(lib):
     assert lib.idx_q_quant(P, 0, 100, 4, 1, 128, 0, P, None, None) == STRIDE
 
 
+def test_fused_producer_checks(lib):
+    c = _cache()
+    kn = lib.idx_k_norm_rope_store
+    # (cache, k, dtype, stride, positions, cos_sin, max_position, rope_dim, weight, eps, slots, N, stream)
+    assert kn(ctypes.byref(c), P, 0, 128, P, P, 16, 3, P, 1e-6, P, 10, None) == SHAPE  # odd rope_dim
+    assert kn(ctypes.byref(c), P, 0, 128, P, P, 16, 130, P, 1e-6, P, 10, None) == SHAPE  # rope_dim > D
+    assert kn(ctypes.byref(c), P, 0, 128, None, P, 16, 64, P, 1e-6, P, 10, None) == NULL
+    assert kn(ctypes.byref(c), P, 0, 128, P, None, 16, 64, P, 1e-6, P, 10, None) == NULL
+    assert kn(ctypes.byref(c), P, 0, 128, P, P, 0, 64, P, 1e-6, P, 10, None) == SHAPE  # empty table
+    assert kn(ctypes.byref(c), P, 0, 128, P, P, 16, 64, P, 0.0, P, 10, None) == SHAPE  # eps must be > 0
+    assert kn(ctypes.byref(c), P, 0, 128, P, P, 16, 64, P + 4, 1e-6, P, 10, None) == STRIDE  # weight alignment
+    assert kn(ctypes.byref(c), P, 0, 128, P + 4, P, 16, 64, P, 1e-6, P, 10, None) == STRIDE  # positions alignment
+    assert kn(ctypes.byref(c), None, 0, 128, None, None, 0, 0, None, 1e-6, None, 0, None) == OK  # N = 0
+    qr = lib.idx_q_rope_quant
+    # (q, dtype, stride, positions, cos_sin, max_position, rope_dim, weights, w_stride, scale, T, H, D, fmt,
+    #  q_out, q_scale_out, weights_out, stream)
+    assert qr(P, 0, 128, P, P, 16, 5, P, 1, 1.0, 4, 1, 128, 0, P, None, P, None) == SHAPE
+    assert qr(P, 0, 128, P, P, 16, 64, None, 1, 1.0, 4, 1, 128, 0, P, None, P, None) == NULL
+    assert qr(P, 0, 128, P, P, 16, 64, P, 1, 1.0, 4, 1, 128, 0, P, None, None, None) == NULL
+    assert qr(P, 0, 128, P, P, 16, 64, P, 0, 1.0, 4, 1, 128, 0, P, None, P, None) == STRIDE  # weights stride < H
+    assert qr(P, 0, 128, P, P, 16, 64, P, 1, 1.0, 4, 1, 128, 0, P + 4, None, P, None) == STRIDE  # fp8 q_out
+    assert qr(P, 0, 128, P, P, 16, 64, P, 1, 1.0, 4, 1, 128, 1, P, None, P, None) == NULL  # MXFP4 needs scales
+    assert qr(None, 0, 128, None, None, 0, 0, None, 1, 1.0, 0, 1, 128, 0, None, None, None, None) == OK  # T = 0
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path; a GPU is visible")
 def test_valid_call_without_device_reports_device_error(lib):
     # arguments pass every host check, so the call reaches the device query, which
