@@ -168,3 +168,39 @@ def topk(logits, starts, ends, k: int) -> np.ndarray:
         chosen = np.sort(cols[order[:k]])
         out[r, : chosen.size] = (chosen - a).astype(np.int32)
     return out
+
+
+def topk_to_slots(topk_idx, row_seq, block_table, page_size: int, row_valid=None):
+    """Top-k rows of local key positions -> a ragged stream of physical cache slots
+    (page ``vllm.v1.attention.ops.rocm_aiter_mla_sparse``,
+    ``build_prefill_topk_ragged_indices``: top-k rows hold positions local to each
+    sequence, mapped through the sequence's block table to compressed-cache slots and
+    packed row after row; page ``vllm.models.deepseek_v41.amd.rocm``,
+    ``_decode_topk_ragged``: the decode rows take the same mapping with the
+    request of each token and its validity flag).
+
+    Position p of row r (sequence b = row_seq[r]) is slot
+    block_table[b, p // page_size] * page_size + p % page_size. Entries < 0 (the -1
+    pads) and positions past the block table are dropped, as are all entries of a row
+    whose valid flag is 0. Returns (slots [total] int32, indptr [rows + 1] int32,
+    lens [rows] int32), the slots of row r at slots[indptr[r]:indptr[r + 1]] in the
+    order of the row's entries.
+    """
+    topk_idx = np.asarray(topk_idx)
+    rows, k = topk_idx.shape
+    bt = np.asarray(block_table)
+    max_blocks = bt.shape[1]
+    out, lens = [], np.zeros(rows, dtype=np.int32)
+    for r in range(rows):
+        if row_valid is not None and not row_valid[r]:
+            continue
+        b = int(row_seq[r])
+        for p in topk_idx[r]:
+            p = int(p)
+            if p < 0 or p >= max_blocks * page_size:
+                continue
+            out.append(int(bt[b, p // page_size]) * page_size + p % page_size)
+            lens[r] += 1
+    indptr = np.zeros(rows + 1, dtype=np.int32)
+    indptr[1:] = np.cumsum(lens)
+    return np.array(out, dtype=np.int32), indptr, lens

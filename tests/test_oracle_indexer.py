@@ -337,3 +337,34 @@ def test_topk_selected_dominate_unselected():
 def test_topk_signed_zero_ties():
     row = np.array([[0.0, -0.0, 0.0, -1.0]])
     assert indexer.topk(row, [0], [4], 2).tolist() == [[0, 1]]
+
+
+def test_topk_to_slots_handworked():
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "handworked_topk_slots.json")))
+    slots, indptr, lens = indexer.topk_to_slots(np.array(g["topk"]), g["row_seq"], np.array(g["block_table"]),
+                                                g["page_size"], g["row_valid"])
+    np.testing.assert_array_equal(slots, g["slots"])
+    np.testing.assert_array_equal(indptr, g["indptr"])
+    np.testing.assert_array_equal(lens, g["lens"])
+
+
+def test_topk_to_slots_inverts_the_page_layout():
+    # a slot names a page entry; reading the block table backwards recovers the
+    # local position from each slot
+    rng = np.random.default_rng(11)
+    P, B, mb = 16, 3, 8
+    perm = rng.permutation(B * mb)
+    bt = perm.reshape(B, mb)
+    topk = rng.integers(-1, P * mb, (6, 10))
+    seq = np.array([0, 0, 1, 1, 2, 2])
+    slots, indptr, lens = indexer.topk_to_slots(topk, seq, bt, P)
+    inv = {int(page): (b, blk) for b in range(B) for blk, page in enumerate(bt[b])}
+    for r in range(6):
+        kept = topk[r][topk[r] >= 0]
+        got = slots[indptr[r]:indptr[r + 1]]
+        assert len(got) == len(kept) == lens[r]
+        for s, p in zip(got, kept):
+            b, blk = inv[int(s) // P]
+            assert b == seq[r] and blk * P + int(s) % P == p
