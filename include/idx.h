@@ -269,6 +269,33 @@ idx_status idx_q_rope_quant(const void *q, int32_t q_dtype, int64_t q_row_stride
                             int32_t fmt, void *q_out, int32_t *q_scale_out, float *weights_out,
                             hipStream_t stream);
 
+/*
+ * idx_topk_to_slots - top-k rows of local key positions to a ragged stream of
+ * physical cache slots, the form the sparse-attention step consumes. Page
+ * "vllm.v1.attention.ops.rocm_aiter_mla_sparse", build_prefill_topk_ragged_indices
+ * (positions local to each sequence mapped through its block table and packed row
+ * after row); page "vllm.models.deepseek_v41.amd.rocm", _decode_topk_ragged (the same
+ * for decode rows, with each row's request and validity flag).
+ *
+ *   topk          [rows, k] int32 (idx_topk's output), row r at topk + r*topk_row_stride.
+ *                 Entries < 0 (pads) and positions >= max_blocks*page_size are dropped.
+ *   row_seq       [rows] int32 or NULL: the sequence of row r (NULL: r / next_n);
+ *                 clamped to [0, B - 1].
+ *   row_valid     [rows] uint8 or NULL: a row whose flag is 0 contributes nothing.
+ *   block_table   [B, max_blocks] int32 with block_table_stride (>= max_blocks);
+ *                 position p of sequence b is slot
+ *                 block_table[b][p / page_size] * page_size + p % page_size.
+ *   slots_out     ragged slots (capacity rows*k int32); row r's slots, in the order
+ *                 of its entries, at slots_out[indptr_out[r] .. indptr_out[r+1]).
+ *   indptr_out    [rows + 1] int32 (indptr_out[0] = 0); lens_out [rows] int32 or NULL.
+ *   Limits: rows, k >= 0; B, max_blocks, page_size >= 1.
+ */
+idx_status idx_topk_to_slots(const int32_t *topk, int64_t topk_row_stride, int32_t rows, int32_t k,
+                             const int32_t *row_seq, int32_t next_n, int32_t B, const uint8_t *row_valid,
+                             const int32_t *block_table, int64_t block_table_stride, int32_t max_blocks,
+                             int32_t page_size, int32_t *slots_out, int32_t *indptr_out, int32_t *lens_out,
+                             hipStream_t stream);
+
 /* Static text naming a status; never NULL. */
 const char *idx_status_str(idx_status s);
 /* IDX_ABI_VERSION of the built library. */

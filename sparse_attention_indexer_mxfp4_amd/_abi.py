@@ -24,6 +24,7 @@ STATUS_NAMES = {
 EXPORTS = (
     "idx_page_bytes", "idx_mqa_logits", "idx_paged_mqa_logits", "idx_paged_mqa_logits_workspace", "idx_topk",
     "idx_topk_workspace", "idx_k_store", "idx_q_quant", "idx_k_norm_rope_store", "idx_q_rope_quant",
+    "idx_topk_to_slots",
     "idx_status_str", "idx_abi_version",
 )
 
@@ -71,6 +72,7 @@ def _declare(lib: ctypes.CDLL) -> None:
         "idx_k_norm_rope_store": (_I32, [cache_p, _P, _I32, _I64, _P, _P, _I32, _I32, _P, _F32, _P, _I32, _P]),
         "idx_q_rope_quant": (_I32, [_P, _I32, _I64, _P, _P, _I32, _I32, _P, _I64, _F32, _I32, _I32, _I32, _I32, _P,
                                     _P, _P, _P]),
+        "idx_topk_to_slots": (_I32, [_P, _I64, _I32, _I32, _P, _I32, _I32, _P, _P, _I64, _I32, _I32, _P, _P, _P, _P]),
         "idx_status_str": (ctypes.c_char_p, [_I32]),
         "idx_abi_version": (_I32, []),
     }

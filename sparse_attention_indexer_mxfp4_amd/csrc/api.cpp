@@ -164,6 +164,22 @@ idx_status idx_q_rope_quant(const void *q, int32_t q_dtype, int64_t q_row_stride
   return launched(idx::launch_q_rope_quant(a, stream));
 }
 
+idx_status idx_topk_to_slots(const int32_t *topk, int64_t topk_row_stride, int32_t rows, int32_t k,
+                             const int32_t *row_seq, int32_t next_n, int32_t B, const uint8_t *row_valid,
+                             const int32_t *block_table, int64_t block_table_stride, int32_t max_blocks,
+                             int32_t page_size, int32_t *slots_out, int32_t *indptr_out, int32_t *lens_out,
+                             hipStream_t stream) {
+  bool empty = false;  // no rows: only indptr[0] = 0 is written
+  idx_status s = idx::check_topk_to_slots(topk, topk_row_stride, rows, k, row_seq, next_n, B, block_table,
+                                          block_table_stride, max_blocks, page_size, slots_out, indptr_out, &empty);
+  if (s != IDX_OK) return s;
+  int cus = 0;
+  if ((s = current_device(&cus)) != IDX_OK) return s;
+  idx::SlotsArgs a{topk, topk_row_stride, rows, k, row_seq, next_n, B, row_valid, block_table, block_table_stride,
+                   max_blocks, page_size, slots_out, indptr_out, lens_out};
+  return launched(idx::launch_topk_to_slots(a, stream));
+}
+
 const char *idx_status_str(idx_status s) {
   switch (s) {
     case IDX_OK: return "IDX_OK";

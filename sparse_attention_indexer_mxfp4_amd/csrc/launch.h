@@ -101,11 +101,27 @@ struct QQuantArgs {
   int32_t *q_scale_out;
 };
 
+struct SlotsArgs {
+  const int32_t *topk;
+  int64_t topk_row_stride;
+  int32_t rows, k;
+  const int32_t *row_seq;
+  int32_t next_n, B;
+  const uint8_t *row_valid;
+  const int32_t *block_table;
+  int64_t block_table_stride;
+  int32_t max_blocks, page_size;
+  int32_t *slots;
+  int32_t *indptr;
+  int32_t *lens;
+};
+
 hipError_t launch_mqa_logits(const MqaArgs &a, int num_cus, hipStream_t stream);
 hipError_t launch_paged_logits(const PagedArgs &a, int num_cus, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs &a, int num_cus, hipStream_t stream);
 hipError_t launch_k_store(const KStoreArgs &a, hipStream_t stream);
 hipError_t launch_q_quant(const QQuantArgs &a, hipStream_t stream);
 hipError_t launch_q_rope_quant(const QRopeArgs &a, hipStream_t stream);
+hipError_t launch_topk_to_slots(const SlotsArgs &a, hipStream_t stream);
 
 }  // namespace idx

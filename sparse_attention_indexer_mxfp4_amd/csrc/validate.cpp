@@ -169,4 +169,25 @@ idx_status check_q_rope_quant(const void *q, int32_t q_dtype, int64_t q_row_stri
   return IDX_OK;
 }
 
+idx_status check_topk_to_slots(const void *topk, int64_t topk_row_stride, int32_t rows, int32_t k,
+                               const void *row_seq, int32_t next_n, int32_t B, const void *block_table,
+                               int64_t block_table_stride, int32_t max_blocks, int32_t page_size,
+                               const void *slots_out, const void *indptr_out, bool *empty) {
+  *empty = false;
+  if (rows < 0 || k < 0 || B < 1 || max_blocks < 1 || page_size < 1) return IDX_ERR_SHAPE;
+  if (!row_seq && next_n < 1) return IDX_ERR_SHAPE;
+  if (!indptr_out) return IDX_ERR_NULL;
+  if (int64_t(max_blocks) * page_size > INT32_MAX) return IDX_ERR_SHAPE;
+  if (rows == 0) {
+    *empty = true;  // indptr is the single 0, written by the launch of the scan
+    return IDX_OK;
+  }
+  if (!topk || !block_table || (k > 0 && !slots_out)) return IDX_ERR_NULL;
+  if (topk_row_stride < k || block_table_stride < max_blocks) return IDX_ERR_STRIDE;
+  if (!aligned(topk, 4) || !aligned(block_table, 4) || !aligned(indptr_out, 4)) return IDX_ERR_STRIDE;
+  if (row_seq && !aligned(row_seq, 4)) return IDX_ERR_STRIDE;
+  if (slots_out && !aligned(slots_out, 4)) return IDX_ERR_STRIDE;
+  return IDX_OK;
+}
+
 }  // namespace idx

@@ -55,4 +55,9 @@ idx_status check_q_rope_quant(const void *q, int32_t q_dtype, int64_t q_row_stri
                               int64_t weights_row_stride, int32_t T, int32_t H, int32_t D, int32_t fmt,
                               const void *q_out, const void *q_scale_out, const void *weights_out, bool *empty);
 
+idx_status check_topk_to_slots(const void *topk, int64_t topk_row_stride, int32_t rows, int32_t k,
+                               const void *row_seq, int32_t next_n, int32_t B, const void *block_table,
+                               int64_t block_table_stride, int32_t max_blocks, int32_t page_size,
+                               const void *slots_out, const void *indptr_out, bool *empty);
+
 }  // namespace idx

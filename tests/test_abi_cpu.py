@@ -191,6 +191,19 @@ def test_fused_producer_checks(lib):
     assert qr(None, 0, 128, None, None, 0, 0, None, 1, 1.0, 0, 1, 128, 0, None, None, None, None) == OK  # T = 0
 
 
+def test_topk_to_slots_checks(lib):
+    f = lib.idx_topk_to_slots
+    # (topk, stride, rows, k, row_seq, next_n, B, row_valid, bt, bt_stride, max_blocks, P, slots, indptr, lens, s)
+    assert f(P, 8, 4, 8, None, 1, 0, None, P, 4, 4, 16, P, P, None, None) == SHAPE  # B < 1
+    assert f(P, 8, 4, 8, None, 0, 2, None, P, 4, 4, 16, P, P, None, None) == SHAPE  # next_n < 1 without row_seq
+    assert f(P, 8, 4, 8, None, 1, 2, None, P, 4, 4, 16, P, None, None, None) == NULL  # indptr
+    assert f(P, 8, 4, 8, None, 1, 2, None, None, 4, 4, 16, P, P, None, None) == NULL  # block table
+    assert f(P, 4, 4, 8, None, 1, 2, None, P, 4, 4, 16, P, P, None, None) == STRIDE  # topk stride < k
+    assert f(P, 8, 4, 8, None, 1, 2, None, P, 3, 4, 16, P, P, None, None) == STRIDE  # bt stride < max_blocks
+    assert f(P + 2, 8, 4, 8, None, 1, 2, None, P, 4, 4, 16, P, P, None, None) == STRIDE
+    assert f(P, 8, -1, 8, None, 1, 2, None, P, 4, 4, 16, P, P, None, None) == SHAPE
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path; a GPU is visible")
 def test_valid_call_without_device_reports_device_error(lib):
     # arguments pass every host check, so the call reaches the device query, which

@@ -60,3 +60,40 @@ def test_topk_many_rows():
     ends = rng.integers(0, width + 1, rows)
     got = _run(L, np.zeros(rows, np.int32), ends, k)
     np.testing.assert_array_equal(got, indexer.topk(L.astype(np.float64), None, ends, k))
+
+
+@pytest.mark.parametrize("next_n,valid", [(1, False), (2, True)])
+def test_topk_to_slots_matches_oracle(next_n, valid):
+    from oracle import indexer as oi
+    rng = np.random.default_rng(410 + next_n)
+    B, P, mb, k = 9, 16, 12, 40
+    rows = B * next_n
+    bt = rng.permutation(B * mb + 5)[:B * mb].reshape(B, mb).astype(np.int32)
+    topk = rng.integers(-1, P * mb + 3, (rows, k)).astype(np.int32)  # pads and out-of-table entries too
+    topk[0, :] = -1
+    rv = (rng.random(rows) > 0.3).astype(np.uint8) if valid else None
+    slots, indptr, lens = ops.idx_topk_to_slots(torch.from_numpy(topk).to(DEV), torch.from_numpy(bt).to(DEV), P,
+                                                next_n=next_n,
+                                                row_valid=None if rv is None else torch.from_numpy(rv).to(DEV))
+    want_s, want_p, want_l = oi.topk_to_slots(topk, np.arange(rows) // next_n, bt, P, rv)
+    ip = indptr.cpu().numpy()
+    np.testing.assert_array_equal(ip, want_p)
+    np.testing.assert_array_equal(lens.cpu().numpy(), want_l)
+    np.testing.assert_array_equal(slots.cpu().numpy()[: ip[-1]], want_s)
+
+
+def test_topk_to_slots_after_topk_and_empty():
+    # the real chain: paged-style rows through idx_topk, then to slots; and no rows
+    rng = np.random.default_rng(420)
+    rows, width, k, P = 6, 300, 32, 16
+    L = torch.from_numpy(rng.standard_normal((rows, width)).astype(np.float32)).to(DEV)
+    ends = torch.tensor([300, 10, 0, 150, 299, 33], dtype=torch.int32, device=DEV)
+    out = ops.idx_topk(L, None, ends, k)
+    bt = torch.from_numpy(rng.permutation(200)[: rows * 19].reshape(rows, 19).astype(np.int32)).to(DEV)
+    slots, indptr, lens = ops.idx_topk_to_slots(out, bt, P)
+    from oracle import indexer as oi
+    want_s, want_p, _ = oi.topk_to_slots(out.cpu().numpy(), np.arange(rows), bt.cpu().numpy(), P)
+    np.testing.assert_array_equal(indptr.cpu().numpy(), want_p)
+    np.testing.assert_array_equal(slots.cpu().numpy()[: want_p[-1]], want_s)
+    e_slots, e_indptr, e_lens = ops.idx_topk_to_slots(torch.zeros((0, k), dtype=torch.int32, device=DEV), bt, P)
+    assert e_indptr.cpu().tolist() == [0] and e_lens.numel() == 0
