@@ -16,8 +16,8 @@
 // neighbouring shares, so a sequence's queries stay in one L2. A wave
 //   - fetches the block-table entries of its next 16 chunks with one vector load
 //     (lane l: chunk l/4, 16-key group l%4) and reads them back with readlane;
-//   - keeps two chunks in registers: the loads of chunk i+1 are in flight while
-//     chunk i is scored;
+//   - keeps kRing chunks in registers: the loads of chunks i+1 .. i+kRing-1 are in
+//     flight while chunk i is scored;
 //   - holds its sequence's queries as MFMA A operands (16 heads x 128 channels per
 //     tile), reloading them when its share crosses into the next sequence.
 // K bytes go straight into MFMA B operands:
@@ -46,7 +46,12 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChunk = 64;
-constexpr int kMinChunksPerWave = 4;
+constexpr int kMinChunksPerWave = 2;
+// Chunks a wave holds: one being scored, the rest in flight. Three where the extra
+// buffer keeps the occupancy the register count allows anyway; two for single-row
+// fp8, where a third buffer would cost a wave per SIMD.
+template <int FMT, int NR>
+constexpr int ring_depth() { return (FMT == 0 && NR == 1) ? 2 : 3; }
 constexpr int kTileStride = 144;  // LDS bytes per key row of a wave's fp8 tile (128 + 16 against bank conflicts)
 
 // Exclusive prefix sum of per-thread values over the workgroup; returns the
@@ -330,62 +335,48 @@ __global__ __launch_bounds__(kThreads) void paged_logits_kernel(PagedArgs a) {
     }
   };
 
-  // ---- stream the share: chunk i+1 in flight while chunk i is scored ------------------
+  // ---- stream the share through a ring of kRing chunk buffers: while chunk i is
+  // scored, chunks i+1 .. i+kRing-1 are in flight -----------------------------------------
   if (u0 < u1) {
     int pg_base = u0;
     int pg = load_pages(pg_base);
-    int b = find_seq(s_pref, a.B, u0);
-    int c = u0 - s_pref[b];
-    Chunk<FMT> bufA, bufB;
-    issue(bufA, pg, 0, b, c);
-    load_queries(b);
-    int qb = b;  // sequence whose queries are loaded
-    // next chunk's coordinates
-    auto advance = [&](int &bb, int &cc) {
-      if (++cc >= s_pref[bb + 1] - s_pref[bb]) {
-        bb = find_seq(s_pref, a.B, s_pref[bb + 1]);
-        cc = 0;
+    int ib = find_seq(s_pref, a.B, u0);  // coordinates of the next chunk to issue
+    int ic = u0 - s_pref[ib];
+    int iu = u0;
+    constexpr int kRing = ring_depth<FMT, NR>();
+    Chunk<FMT> ring[kRing];
+    int rb[kRing], rc[kRing];  // sequence and chunk index held by each ring slot
+    auto issue_next = [&](Chunk<FMT> &slot_buf, int &slot_b, int &slot_c) {
+      if (iu - pg_base >= 16) {
+        pg_base = iu;
+        pg = load_pages(pg_base);
+      }
+      issue(slot_buf, pg, iu - pg_base, ib, ic);
+      slot_b = ib;
+      slot_c = ic;
+      if (++iu < u1 && ++ic >= s_pref[ib + 1] - s_pref[ib]) {
+        ib = find_seq(s_pref, a.B, s_pref[ib + 1]);
+        ic = 0;
       }
     };
-    for (int u = u0; u < u1; u += 2) {
-      // chunk u in bufA (coordinates b, c); prefetch chunk u + 1 into bufB
-      int b1 = b, c1 = c;
-      const bool has1 = u + 1 < u1;
-      if (has1) {
-        advance(b1, c1);
-        if (u + 1 - pg_base >= 16) {
-          pg_base = u + 1;
-          pg = load_pages(pg_base);
+#pragma unroll
+    for (int s = 0; s < kRing - 1; ++s)
+      if (iu < u1) issue_next(ring[s], rb[s], rc[s]);
+    int qb = -1;  // sequence whose queries are loaded
+    for (int u = u0; u < u1; u += kRing) {
+#pragma unroll
+      for (int s = 0; s < kRing; ++s) {
+        if (u + s >= u1) break;
+        const int nxt = (s + kRing - 1) % kRing;  // slot of chunk u + s + kRing - 1
+        if (iu < u1) issue_next(ring[nxt], rb[nxt], rc[nxt]);
+        if (rb[s] != qb) {
+          load_queries(rb[s]);
+          qb = rb[s];
         }
-        issue(bufB, pg, u + 1 - pg_base, b1, c1);
+        score(ring[s], rb[s], rc[s]);
       }
-      if (b != qb) {
-        load_queries(b);
-        qb = b;
-      }
-      score(bufA, b, c);
-      if (!has1) break;
-      // chunk u + 1 in bufB; prefetch chunk u + 2 into bufA
-      int b2 = b1, c2 = c1;
-      const bool has2 = u + 2 < u1;
-      if (has2) {
-        advance(b2, c2);
-        if (u + 2 - pg_base >= 16) {
-          pg_base = u + 2;
-          pg = load_pages(pg_base);
-        }
-        issue(bufA, pg, u + 2 - pg_base, b2, c2);
-      }
-      if (b1 != qb) {
-        load_queries(b1);
-        qb = b1;
-      }
-      score(bufB, b1, c1);
-      b = b2;
-      c = c2;
     }
   }
-
 }
 
 // Persistent grid: as many workgroups as can be resident at once (a multiple of 8,
