@@ -285,26 +285,26 @@ def main():
     stream = torch.cuda.current_stream()
 
     # (1) per-kernel durations with HIP events on the launch stream: the K launches of
-    # each kernel back to back between two events (one event pair per kernel costs a
-    # few microseconds of its own, as much as a decode launch). A burst of large
-    # memsets first keeps the GPU busy while the host enqueues, so the events bracket
-    # back-to-back kernels rather than host launch gaps.
-    spin = torch.empty(256 * 2**20, dtype=torch.uint8, device=dev)
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    torch.cuda.synchronize()
-    for _ in range(2 * args.steps + 4):
-        spin.zero_()
-    e[0].record(stream)
-    for i in range(args.steps):
-        logits_call(i)
-    e[1].record(stream)
-    for i in range(args.steps):
-        topk_call()
-    e[2].record(stream)
-    torch.cuda.synchronize()
-    logits_ms = e[0].elapsed_time(e[1]) / args.steps
-    topk_ms = e[1].elapsed_time(e[2]) / args.steps
-    del spin
+    # each kernel captured back to back in a HIP graph of their own, one untimed
+    # replay, then one replay between two events (an event pair per launch would cost
+    # as much as a decode launch, and launches enqueued from Python could leave the
+    # GPU idle between kernels)
+    def timed_replay(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(args.steps):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        g.replay()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / args.steps
+
+    logits_ms = timed_replay(logits_call)
+    topk_ms = timed_replay(lambda i: topk_call())
 
     # (2) whole-step throughput: the K timed steps captured in one HIP graph (the
     # calls neither allocate nor synchronise) and replayed once, so the host's
@@ -350,7 +350,7 @@ def main():
         "dtype": "fp8" if wl_fmt(wl, cfg) == "fp8" else "fp4",
         "data": "synthetic",
         "config": {"workload": wl.name, "config": cfg, "keys_per_step": keys, "topk": wl.topk,
-                   "timing": "K steps in one HIP graph; per-kernel times from HIP events around K back-to-back launches",
+                   "timing": "K steps in one HIP graph; per-kernel times from HIP events around a graph of K back-to-back launches of that kernel",
                    "logits_ms": round(logits_ms, 4), "topk_ms": round(topk_ms, 4),
                    "kstore_ms": None if kstore_ms is None else round(kstore_ms, 4), "k_cache_copies": copies},
         "roofline": roof,
