@@ -35,7 +35,9 @@
 // the chunk in lane L, scales by the key's fp32 scale (fp8; k_scale > 0 so it factors
 // out of the ReLU) and stores one 256-byte segment per row and chunk. Every wave also
 // writes an equal share of the -inf tail (columns past the last chunk of each row's
-// sequence) with 16-byte stores, issued before its K loads.
+// sequence) with 16-byte streaming stores, a few units after each chunk's K loads are
+// issued (and the rest after its last chunk).
+#include <climits>
 #include <mutex>
 
 #include "device.h"
@@ -47,11 +49,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunk = 64;
 constexpr int kMinChunksPerWave = 2;
-// Chunks a wave holds: one being scored, the rest in flight. Three where the extra
-// buffer keeps the occupancy the register count allows anyway; two for single-row
-// fp8, where a third buffer would cost a wave per SIMD.
+// Chunks a wave holds: one being scored, the rest in flight. Three for multi-row
+// (MTP) steps, whose register count allows two waves per SIMD either way; two for
+// single rows, where a third buffer would cost a wave per SIMD.
 template <int FMT, int NR>
-constexpr int ring_depth() { return (FMT == 0 && NR == 1) ? 2 : 3; }
+constexpr int ring_depth() { return NR == 1 ? 2 : 3; }
 constexpr int kTileStride = 144;  // LDS bytes per key row of a wave's fp8 tile (128 + 16 against bank conflicts)
 
 // Exclusive prefix sum of per-thread values over the workgroup; returns the
@@ -114,7 +116,7 @@ struct Chunk<1> {
 };
 
 template <int FMT, int HT, int NR>
-__global__ __launch_bounds__(kThreads) void paged_logits_kernel(PagedArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 1 ? 3 : 1))) void paged_logits_kernel(PagedArgs a) {
   extern __shared__ int s_lds[];  // pref[B + 1], len[B]
   __shared__ int s_scan[kThreads / 64];
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[FMT == 0 ? kThreads / 64 : 1][FMT == 0 ? kChunk * kTileStride : 16];
@@ -178,26 +180,29 @@ __global__ __launch_bounds__(kThreads) void paged_logits_kernel(PagedArgs a) {
   const int u1 = owner ? int(int64_t(U) * (k + 1) / used) : U;
   const float ninf = neg_inf();
 
-  // ---- -inf past each sequence's last chunk (issued first: the stores drain while
-  // the K loads below are in flight) ---------------------------------------------------
-  {
-    const int NU = (a.width + 255) / 256;
-    const int64_t R = int64_t(a.B) * NR;
-    for (int64_t f = v; f < R * NU; f += V) {
-      const int64_t r = f / NU;
-      const int col = int(f % NU) * 256 + lane * 4;
+  // ---- -inf past each sequence's last chunk ------------------------------------------
+  // The wave's share of 256-column units is written a few units at a time, each batch
+  // after a chunk's K loads are issued: memory operations complete in issue order, so
+  // stores issued ahead of the block-table and K loads would delay them.
+  const int fill_nu = (a.width + 255) / 256;
+  const int64_t fill_total = int64_t(a.B) * NR * fill_nu;
+  int64_t fill_next = v;  // next unit of this wave
+  auto fill_some = [&](int units) {
+    for (int i = 0; i < units && fill_next < fill_total; ++i, fill_next += V) {
+      const int64_t r = fill_next / fill_nu;
+      const int col = int(fill_next % fill_nu) * 256 + lane * 4;
       const int bb = int(r / NR);
       const int tail = (s_pref[bb + 1] - s_pref[bb]) * kChunk;
       if (col >= tail && col < a.width) {
         float *p = a.logits + r * a.logits_row_stride + col;
         if (col + 4 <= a.width) {
-          *reinterpret_cast<v4f *>(p) = v4f{ninf, ninf, ninf, ninf};
+          __builtin_nontemporal_store(v4f{ninf, ninf, ninf, ninf}, reinterpret_cast<v4f *>(p));
         } else {
-          for (int i = 0; col + i < a.width; ++i) p[i] = ninf;
+          for (int e = 0; col + e < a.width; ++e) __builtin_nontemporal_store(ninf, p + e);
         }
       }
     }
-  }
+  };
 
   // block-table entries of chunks [base, base + 16): lane l holds chunk base + l/4,
   // 16-key group l%4 (0 past the wave's share or the sequence's end)
@@ -337,7 +342,9 @@ __global__ __launch_bounds__(kThreads) void paged_logits_kernel(PagedArgs a) {
 
   // ---- stream the share through a ring of kRing chunk buffers: while chunk i is
   // scored, chunks i+1 .. i+kRing-1 are in flight -----------------------------------------
-  if (u0 < u1) {
+  int qb = -1;  // sequence whose queries are loaded
+  auto stream = [&](const int u0, const int u1) {
+    if (u0 >= u1) return;
     int pg_base = u0;
     int pg = load_pages(pg_base);
     int ib = find_seq(s_pref, a.B, u0);  // coordinates of the next chunk to issue
@@ -362,13 +369,13 @@ __global__ __launch_bounds__(kThreads) void paged_logits_kernel(PagedArgs a) {
 #pragma unroll
     for (int s = 0; s < kRing - 1; ++s)
       if (iu < u1) issue_next(ring[s], rb[s], rc[s]);
-    int qb = -1;  // sequence whose queries are loaded
     for (int u = u0; u < u1; u += kRing) {
 #pragma unroll
       for (int s = 0; s < kRing; ++s) {
         if (u + s >= u1) break;
         const int nxt = (s + kRing - 1) % kRing;  // slot of chunk u + s + kRing - 1
         if (iu < u1) issue_next(ring[nxt], rb[nxt], rc[nxt]);
+        fill_some(2);
         if (rb[s] != qb) {
           load_queries(rb[s]);
           qb = rb[s];
@@ -376,7 +383,9 @@ __global__ __launch_bounds__(kThreads) void paged_logits_kernel(PagedArgs a) {
         score(ring[s], rb[s], rc[s]);
       }
     }
-  }
+  };
+  stream(u0, u1);
+  fill_some(INT_MAX);
 }
 
 // Persistent grid: as many workgroups as can be resident at once (a multiple of 8,
