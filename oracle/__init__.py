@@ -15,7 +15,10 @@ the method fixes another precision:
 * ``indexer`` - the logits I[t, s] = sum_h w[t, h] * ReLU(q[t, h, :] . k[s, :]) with each
   row's validity mask, the row ends of a paged decode / MTP step, and per-row top-k;
 * ``producers`` - what feeds the path: RMSNorm and RoPE of the keys before the store,
-  RoPE of the queries and the scaling of the weights.
+  RoPE of the queries and the scaling of the weights;
+* ``candidates`` - the two-level indexer: block scores of a source layer's logits, the
+  candidate pool they select, the masked and gathered consumers and the remap of
+  pool slots to positions.
 
 Sources are the vLLM API pages ``vllm.v1.attention.ops.rocm_aiter_mla_sparse``,
 ``vllm.models.deepseek_v41.amd.rocm``, ``vllm.v1.attention.backends.mla.rocm_aiter_mla``
@@ -23,4 +26,4 @@ and ``vllm.v1.attention.ops.rocm_paged_mxfp4_indexer``; each function names the
 section it follows.
 """
 
-from . import cache, formats, indexer, producers  # noqa: F401
+from . import cache, candidates, formats, indexer, producers  # noqa: F401
