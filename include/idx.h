@@ -296,6 +296,114 @@ idx_status idx_topk_to_slots(const int32_t *topk, int64_t topk_row_stride, int32
                              int32_t page_size, int32_t *slots_out, int32_t *indptr_out, int32_t *lens_out,
                              hipStream_t stream);
 
+/*
+ * Two-level indexer. Page "vllm.v1.attention.ops.rocm_paged_mxfp4_indexer": a candidate
+ * source layer takes block maxima from the same walk that writes its logits
+ * (rocm_mxfp4_sparse_attn_indexer with candidate_write; block scores sized
+ * [rows, ceil(width / block)] fp32 by reserve_rocm_mxfp4_indexer_workspace); the
+ * candidate pool is resolved from them once per step; consumer layers either run the
+ * dense walk masked to the pool or score only the pool (rocm_mxfp4_sparse_mqa_indexer),
+ * and a top-k over a pool is turned back into positions (_remap_compact_topk). Page
+ * "vllm.v1.attention.ops.rocm_aiter_mla_sparse", _apply_candidate_mask_strided: the
+ * mask over [0, end) with row_repeat query rows per candidate row. The pages show the
+ * interfaces, not how the pool is chosen; here it is each row's n_cand best blocks.
+ *
+ * A candidate list is int32 [rows / row_repeat, n_cand] (row c at cand + c*cand_row_stride,
+ * 4-byte aligned): block indices, block b covering positions [b*block_size,
+ * (b+1)*block_size). Query row r uses candidate row r / row_repeat.
+ */
+
+/*
+ * idx_paged_mqa_logits_block_max - idx_paged_mqa_logits that also writes each row's
+ * block maxima from the same walk (the candidate source).
+ *
+ *   All arguments up to row_end_out and the workspace are as idx_paged_mqa_logits.
+ *   block_max     [B*next_n, ceil(width / block_size)] fp32, row r at
+ *                 block_max + r*block_max_row_stride (>= ceil(width / block_size)):
+ *                 entry j is the largest logit of columns [j*block_size,
+ *                 (j+1)*block_size) below the row's end, -inf when there is none.
+ *   block_size    16, 32 or 64 (0: no block maxima, block_max ignored).
+ */
+idx_status idx_paged_mqa_logits_block_max(const idx_paged_cache *cache, const void *q, const int32_t *q_scale,
+                                          const float *w, const int32_t *context_lens, int32_t ctx_per_row,
+                                          const int32_t *block_table, int64_t block_table_stride,
+                                          int32_t max_blocks, int32_t B, int32_t next_n, int32_t H, float *logits,
+                                          int64_t logits_row_stride, int32_t width, int32_t *row_end_out,
+                                          float *block_max, int64_t block_max_row_stride, int32_t block_size,
+                                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * idx_candidate_blocks - the candidate pool: per row, the n_cand blocks with the
+ * largest block maxima, ties to the lower block, listed in ascending block order and
+ * padded with -1. It is idx_topk over the block maxima with each row's end rounded up
+ * to blocks.
+ *
+ *   block_max     [rows, num_blocks] fp32 with block_max_row_stride (>= num_blocks).
+ *   row_end       [rows] int32: the rows' logits ends (columns, e.g. the row_end_out of
+ *                 the source call); row r considers blocks [0, ceil(row_end[r] / block_size)).
+ *   block_size    a power of two.
+ *   cand_out      [rows, n_cand] int32 with cand_row_stride (>= n_cand). A row whose end
+ *                 covers b blocks gets min(n_cand, b) entries, then -1.
+ *   workspace     as idx_topk (idx_topk_workspace(rows, num_blocks, n_cand) bytes).
+ */
+idx_status idx_candidate_blocks(const float *block_max, int64_t block_max_row_stride, int32_t rows,
+                                int32_t num_blocks, const int32_t *row_end, int32_t block_size, int32_t n_cand,
+                                int32_t *cand_out, int64_t cand_row_stride, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * idx_apply_candidate_mask - a dense logits row restricted to its pool, in place:
+ * every column c < row_end[r] whose block c / block_size is not in the row's candidate
+ * list becomes -inf (columns at or past the end are left alone).
+ *
+ *   logits        [rows, width] fp32, 16-byte aligned, logits_row_stride a multiple of 4.
+ *   row_end       [rows] int32, clamped to [0, width].
+ *   cand ...      a candidate list (see above); entries < 0 or past the end are ignored.
+ *   block_size    a power of two with ceil(width / block_size) < 65536.
+ */
+idx_status idx_apply_candidate_mask(float *logits, int64_t logits_row_stride, int32_t rows, int32_t width,
+                                    const int32_t *row_end, const int32_t *cand, int64_t cand_row_stride,
+                                    int32_t n_cand, int32_t block_size, int32_t row_repeat, hipStream_t stream);
+
+/*
+ * idx_paged_mqa_logits_gather - the candidate consumer that scores only its pool: pool
+ * slot j of row r holds the logit of position p = cand[j / block_size]*block_size +
+ * j % block_size of row r's sequence (computed exactly as idx_paged_mqa_logits computes
+ * that position's logit), or -inf when the entry is < 0 or p is at or past the row's
+ * end. Any list works; the walk covers each row's slots up to the last one that names a
+ * position, which for a list as idx_candidate_blocks writes it (ascending, then -1) is
+ * nearly the whole list for long rows and little of it for short ones.
+ *
+ *   cache ... H   as idx_paged_mqa_logits (rows r = b*next_n + j, same row ends).
+ *   cand ...      a candidate list (see above); block_size a power of two, >= 16.
+ *   pool_logits   [B*next_n, n_cand*block_size] fp32, 16-byte aligned,
+ *                 pool_row_stride a multiple of 4; every slot is written.
+ *   pool_end_out  [B*next_n] int32, required: one past the row's last slot that names a
+ *                 position (the row end for idx_topk over the pool). A first small
+ *                 kernel writes it and the walk reads it back.
+ *   Limits: B*next_n <= 8192.
+ */
+idx_status idx_paged_mqa_logits_gather(const idx_paged_cache *cache, const void *q, const int32_t *q_scale,
+                                       const float *w, const int32_t *context_lens, int32_t ctx_per_row,
+                                       const int32_t *block_table, int64_t block_table_stride, int32_t max_blocks,
+                                       int32_t B, int32_t next_n, int32_t H, const int32_t *cand,
+                                       int64_t cand_row_stride, int32_t n_cand, int32_t block_size,
+                                       int32_t row_repeat, float *pool_logits, int64_t pool_row_stride,
+                                       int32_t *pool_end_out, hipStream_t stream);
+
+/*
+ * idx_remap_compact_topk - a top-k over pool slots to positions, in place: an entry
+ * j >= 0 becomes cand[j / block_size]*block_size + j % block_size of its row's
+ * candidate row; -1 stays -1, and so does an entry whose candidate is -1 or lies past
+ * the list.
+ *
+ *   topk          [rows, k] int32 with topk_row_stride (>= k).
+ *   cand ...      the candidate list the pool was gathered with; block_size a power of two.
+ */
+idx_status idx_remap_compact_topk(int32_t *topk, int64_t topk_row_stride, int32_t rows, int32_t k,
+                                  const int32_t *cand, int64_t cand_row_stride, int32_t n_cand, int32_t block_size,
+                                  int32_t row_repeat, hipStream_t stream);
+
 /* Static text naming a status; never NULL. */
 const char *idx_status_str(idx_status s);
 /* IDX_ABI_VERSION of the built library. */

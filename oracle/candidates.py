@@ -34,7 +34,8 @@ maxima, nor the bodies of these kernels. Readings taken here:
   least k of the row's positions; below that, the masked route fills up with -inf
   columns outside the pool while the gather route pads with -1;
 * remap: a top-k entry j >= 0 over the pool becomes cand[j // block] * block + j % block,
-  i.e. the start of its pool block plus the offset; -1 stays -1.
+  i.e. the start of its pool block plus the offset; -1 stays -1, and so does an entry
+  whose candidate is -1 or that lies past the list (j >= n * block).
 
 All of it is selection and bookkeeping over given logits: no arithmetic beyond max.
 """
@@ -135,7 +136,7 @@ def remap_compact_topk(topk_idx, cand, block: int, row_repeat: int = 1) -> np.nd
     for r in range(t.shape[0]):
         for i, j in enumerate(t[r]):
             j = int(j)
-            if j < 0:
+            if j < 0 or j // block >= cand.shape[1]:
                 continue
             b = int(cand[r // row_repeat, j // block])
             if b >= 0:

@@ -68,27 +68,149 @@ size_t idx_paged_mqa_logits_workspace(int32_t B, int32_t next_n, int32_t H, cons
   return idx::paged_workspace_bytes(B, next_n, H, cache);
 }
 
+namespace {
+idx::PagedArgs paged_args(const idx_paged_cache *cache, const void *q, const int32_t *q_scale, const float *w,
+                          const int32_t *context_lens, int32_t ctx_per_row, const int32_t *block_table,
+                          int64_t block_table_stride, int32_t max_blocks, int32_t B, int32_t next_n, int32_t H,
+                          float *logits, int64_t logits_row_stride, int32_t width, int32_t *row_end_out) {
+  int shift = -1;
+  for (int sh = 4; sh <= 10; ++sh)
+    if (cache->page_size == (1 << sh)) shift = sh;
+  idx::PagedArgs a{};
+  a.base = static_cast<const uint8_t *>(cache->base);
+  a.page_stride = cache->page_stride_bytes;
+  a.page_size = cache->page_size;
+  a.page_shift = shift;
+  a.num_pages = cache->num_pages;
+  a.fmt = cache->fmt;
+  a.q = static_cast<const uint8_t *>(q);
+  a.q_scale = q_scale;
+  a.w = w;
+  a.context_lens = context_lens;
+  a.ctx_per_row = ctx_per_row != 0;
+  a.block_table = block_table;
+  a.block_table_stride = block_table_stride;
+  a.max_blocks = max_blocks;
+  a.B = B;
+  a.next_n = next_n;
+  a.H = H;
+  a.logits = logits;
+  a.logits_row_stride = logits_row_stride;
+  a.width = width;
+  a.row_end_out = row_end_out;
+  return a;
+}
+}  // namespace
+
 idx_status idx_paged_mqa_logits(const idx_paged_cache *cache, const void *q, const int32_t *q_scale,
                                 const float *w, const int32_t *context_lens, int32_t ctx_per_row,
                                 const int32_t *block_table, int64_t block_table_stride, int32_t max_blocks,
                                 int32_t B, int32_t next_n, int32_t H, float *logits, int64_t logits_row_stride,
                                 int32_t width, int32_t *row_end_out, void *workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
+  return idx_paged_mqa_logits_block_max(cache, q, q_scale, w, context_lens, ctx_per_row, block_table,
+                                        block_table_stride, max_blocks, B, next_n, H, logits, logits_row_stride,
+                                        width, row_end_out, nullptr, 0, 0, workspace, workspace_bytes, stream);
+}
+
+idx_status idx_paged_mqa_logits_block_max(const idx_paged_cache *cache, const void *q, const int32_t *q_scale,
+                                          const float *w, const int32_t *context_lens, int32_t ctx_per_row,
+                                          const int32_t *block_table, int64_t block_table_stride,
+                                          int32_t max_blocks, int32_t B, int32_t next_n, int32_t H, float *logits,
+                                          int64_t logits_row_stride, int32_t width, int32_t *row_end_out,
+                                          float *block_max, int64_t block_max_row_stride, int32_t block_size,
+                                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
   bool empty = false;
   idx_status s = idx::check_paged_mqa_logits(cache, q, q_scale, w, context_lens, block_table, block_table_stride,
                                              max_blocks, B, next_n, H, logits, logits_row_stride, width,
                                              workspace, workspace_bytes, &empty);
+  if (s != IDX_OK) return s;
+  if (block_size != 0 && (s = idx::check_block_max(block_max, block_max_row_stride, block_size, width)) != IDX_OK)
+    return s;
+  if (empty) return IDX_OK;
+  int cus = 0;
+  if ((s = current_device(&cus)) != IDX_OK) return s;
+  idx::PagedArgs a = paged_args(cache, q, q_scale, w, context_lens, ctx_per_row, block_table, block_table_stride,
+                                max_blocks, B, next_n, H, logits, logits_row_stride, width, row_end_out);
+  if (block_size != 0) {
+    a.block_max = block_max;
+    a.block_max_row_stride = block_max_row_stride;
+    a.block_size = block_size;
+  }
+  return launched(idx::launch_paged_logits(a, cus, stream));
+}
+
+idx_status idx_paged_mqa_logits_gather(const idx_paged_cache *cache, const void *q, const int32_t *q_scale,
+                                       const float *w, const int32_t *context_lens, int32_t ctx_per_row,
+                                       const int32_t *block_table, int64_t block_table_stride, int32_t max_blocks,
+                                       int32_t B, int32_t next_n, int32_t H, const int32_t *cand,
+                                       int64_t cand_row_stride, int32_t n_cand, int32_t block_size,
+                                       int32_t row_repeat, float *pool_logits, int64_t pool_row_stride,
+                                       int32_t *pool_end_out, hipStream_t stream) {
+  idx_status s = idx::check_candidate_list(cand, cand_row_stride, n_cand, block_size, row_repeat);
+  if (s != IDX_OK) return s;
+  if ((s = idx::check_gather(B, next_n, block_size, pool_logits, pool_row_stride, n_cand, pool_end_out)) != IDX_OK)
+    return s;
+  const int32_t width = n_cand * block_size;
+  bool empty = false;
+  s = idx::check_paged_mqa_logits(cache, q, q_scale, w, context_lens, block_table, block_table_stride, max_blocks,
+                                  B, next_n, H, pool_logits, pool_row_stride, width, nullptr, 0, &empty);
   if (s != IDX_OK || empty) return s;
   int cus = 0;
   if ((s = current_device(&cus)) != IDX_OK) return s;
-  int shift = -1;
-  for (int sh = 4; sh <= 10; ++sh)
-    if (cache->page_size == (1 << sh)) shift = sh;
-  idx::PagedArgs a{static_cast<const uint8_t *>(cache->base), cache->page_stride_bytes, cache->page_size, shift,
-                   cache->num_pages, cache->fmt, static_cast<const uint8_t *>(q), q_scale, w, context_lens,
-                   ctx_per_row != 0, block_table, block_table_stride, max_blocks, B, next_n, H, logits,
-                   logits_row_stride, width, row_end_out};
+  idx::PagedArgs a = paged_args(cache, q, q_scale, w, context_lens, ctx_per_row, block_table, block_table_stride,
+                                max_blocks, B, next_n, H, pool_logits, pool_row_stride, width, pool_end_out);
+  a.block_size = block_size;
+  a.cand = cand;
+  a.cand_row_stride = cand_row_stride;
+  a.n_cand = n_cand;
+  a.row_repeat = row_repeat;
   return launched(idx::launch_paged_logits(a, cus, stream));
+}
+
+idx_status idx_candidate_blocks(const float *block_max, int64_t block_max_row_stride, int32_t rows,
+                                int32_t num_blocks, const int32_t *row_end, int32_t block_size, int32_t n_cand,
+                                int32_t *cand_out, int64_t cand_row_stride, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  if (block_size < 1 || (block_size & (block_size - 1))) return IDX_ERR_SHAPE;
+  bool empty = false;
+  idx_status s = idx::check_topk(block_max, block_max_row_stride, rows, num_blocks, row_end, n_cand, cand_out,
+                                 cand_row_stride, workspace, workspace_bytes, &empty);
+  if (s != IDX_OK || empty) return s;
+  int cus = 0;
+  if ((s = current_device(&cus)) != IDX_OK) return s;
+  idx::TopkArgs a{block_max, block_max_row_stride, rows, num_blocks, nullptr, row_end, n_cand, cand_out,
+                  cand_row_stride, block_size};
+  return launched(idx::launch_topk(a, cus, stream));
+}
+
+idx_status idx_apply_candidate_mask(float *logits, int64_t logits_row_stride, int32_t rows, int32_t width,
+                                    const int32_t *row_end, const int32_t *cand, int64_t cand_row_stride,
+                                    int32_t n_cand, int32_t block_size, int32_t row_repeat, hipStream_t stream) {
+  bool empty = false;
+  idx_status s = idx::check_candidate_mask(logits, logits_row_stride, rows, width, row_end, block_size, &empty);
+  if (s != IDX_OK) return s;
+  if ((s = idx::check_candidate_list(cand, cand_row_stride, n_cand, block_size, row_repeat)) != IDX_OK) return s;
+  if (empty) return IDX_OK;
+  int cus = 0;
+  if ((s = current_device(&cus)) != IDX_OK) return s;
+  idx::MaskArgs a{logits, logits_row_stride, rows, width, row_end, cand, cand_row_stride, n_cand, block_size,
+                  row_repeat};
+  return launched(idx::launch_candidate_mask(a, stream));
+}
+
+idx_status idx_remap_compact_topk(int32_t *topk, int64_t topk_row_stride, int32_t rows, int32_t k,
+                                  const int32_t *cand, int64_t cand_row_stride, int32_t n_cand, int32_t block_size,
+                                  int32_t row_repeat, hipStream_t stream) {
+  bool empty = false;
+  idx_status s = idx::check_remap(topk, topk_row_stride, rows, k, &empty);
+  if (s != IDX_OK) return s;
+  if ((s = idx::check_candidate_list(cand, cand_row_stride, n_cand, block_size, row_repeat)) != IDX_OK) return s;
+  if (empty) return IDX_OK;
+  int cus = 0;
+  if ((s = current_device(&cus)) != IDX_OK) return s;
+  idx::RemapArgs a{topk, topk_row_stride, rows, k, cand, cand_row_stride, n_cand, block_size, row_repeat};
+  return launched(idx::launch_remap_compact_topk(a, stream));
 }
 
 size_t idx_topk_workspace(int32_t rows, int32_t width, int32_t k) { return idx::topk_workspace_bytes(rows, width, k); }
@@ -102,7 +224,7 @@ idx_status idx_topk(const float *logits, int64_t logits_row_stride, int32_t rows
   if (s != IDX_OK || empty) return s;
   int cus = 0;
   if ((s = current_device(&cus)) != IDX_OK) return s;
-  idx::TopkArgs a{logits, logits_row_stride, rows, width, row_start, row_end, k, out, out_row_stride};
+  idx::TopkArgs a{logits, logits_row_stride, rows, width, row_start, row_end, k, out, out_row_stride, 1};
   return launched(idx::launch_topk(a, cus, stream));
 }
 

@@ -42,6 +42,16 @@ struct PagedArgs {
   int64_t logits_row_stride;
   int32_t width;
   int32_t *row_end_out;
+  // dense walk: block maxima of every row (block_max != nullptr), block_size 16, 32 or 64
+  float *block_max;
+  int64_t block_max_row_stride;
+  int32_t block_size;  // also the pool block of the gather walk
+  // gather walk (cand != nullptr): row r scores only its candidate pool, slot j being
+  // position cand[r / row_repeat][j / block_size] * block_size + j % block_size
+  const int32_t *cand;
+  int64_t cand_row_stride;
+  int32_t n_cand;
+  int32_t row_repeat;
 };
 
 struct TopkArgs {
@@ -53,6 +63,26 @@ struct TopkArgs {
   int32_t k;
   int32_t *out;
   int64_t out_row_stride;
+  int32_t end_div;  // the row end used is ceil(row_end[r] / end_div) (1: row_end itself)
+};
+
+struct MaskArgs {
+  float *logits;
+  int64_t logits_row_stride;
+  int32_t rows, width;
+  const int32_t *row_end;
+  const int32_t *cand;
+  int64_t cand_row_stride;
+  int32_t n_cand, block_size, row_repeat;
+};
+
+struct RemapArgs {
+  int32_t *topk;
+  int64_t topk_row_stride;
+  int32_t rows, k;
+  const int32_t *cand;
+  int64_t cand_row_stride;
+  int32_t n_cand, block_size, row_repeat;
 };
 
 struct KStoreArgs {
@@ -123,5 +153,7 @@ hipError_t launch_k_store(const KStoreArgs &a, hipStream_t stream);
 hipError_t launch_q_quant(const QQuantArgs &a, hipStream_t stream);
 hipError_t launch_q_rope_quant(const QRopeArgs &a, hipStream_t stream);
 hipError_t launch_topk_to_slots(const SlotsArgs &a, hipStream_t stream);
+hipError_t launch_candidate_mask(const MaskArgs &a, hipStream_t stream);
+hipError_t launch_remap_compact_topk(const RemapArgs &a, hipStream_t stream);
 
 }  // namespace idx

@@ -37,6 +37,19 @@
 // writes an equal share of the -inf tail (columns past the last chunk of each row's
 // sequence) with 16-byte streaming stores, a few units after each chunk's K loads are
 // issued (and the rest after its last chunk).
+//
+// Two-level indexer (page "vllm.v1.attention.ops.rocm_paged_mxfp4_indexer", module
+// description and rocm_mxfp4_sparse_mqa_indexer):
+//   - block maxima: the candidate source's walk also reduces each chunk's stored
+//     logits to the maxima of its 16-, 32- or 64-key blocks (lane shuffles) and
+//     stores one value per block; blocks past a sequence's chunks get -inf with the
+//     tail;
+//   - gather walk: a consumer row scores only its candidate pool. Each query row is
+//     its own walk (NR = 1) over pool slots; a 16-key group of slots lies inside one
+//     pool block and so at 16 consecutive positions of one page, found through the
+//     candidate entry and then the block table. Keys of a group whose candidate is
+//     -1 or past the row's end are not loaded and score -inf. A first one-wave-per-row
+//     kernel finds each row's pool length, which the walk uses as its sequence length.
 #include <climits>
 #include <mutex>
 
@@ -104,24 +117,71 @@ __device__ __forceinline__ void row_ends(const PagedArgs &a, int b, int cap, int
 // LDS tile at scoring time. MXFP4: kb[kg] is already the B operand of key group kg.
 template <int FMT>
 struct Chunk;
+// The gather walk also keeps, per 16-key group, the position of its first key (-1 for
+// a group that names no key of the row).
 template <>
 struct Chunk<0> {
   v4i raw[8];
   float ksc;
+  int gpos[4];
 };
 template <>
 struct Chunk<1> {
   v8i kb[4];
   int ksb[4];
+  int gpos[4];
 };
 
-template <int FMT, int HT, int NR>
+// Gather walk: the row's own end (exclusive), as for the dense walk
+__device__ __forceinline__ int gather_row_end(const PagedArgs &a, int r, int cap) {
+  const int nn = a.next_n;
+  const int e = a.ctx_per_row ? a.context_lens[r] : a.context_lens[r / nn] - nn + r % nn + 1;
+  return min(max(e, 0), cap);
+}
+
+// Gather walk, first pass (one wave per row): the pool length, one past the last slot
+// that names a position below the row's end. Entry i of the candidate list names one
+// iff 0 <= cand[i] < ceil(end / block); the last such entry i holds slots
+// [i * block, i * block + min(block, end - cand[i] * block)). Written to row_end_out,
+// from which the walk reads it back.
+__global__ __launch_bounds__(64) void pool_length_kernel(PagedArgs a) {
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int bs = a.block_size;
+  const int bsh = 31 - __builtin_clz(bs);
+  const int e = gather_row_end(a, r, int(min(int64_t(INT_MAX), int64_t(a.max_blocks) * a.page_size)));
+  const int nbe = (e >> bsh) + ((e & (bs - 1)) != 0);
+  const int32_t *cr = a.cand + int64_t(r / a.row_repeat) * a.cand_row_stride;
+  int last = -1, blk = 0;
+  for (int i = lane; i < a.n_cand; i += 64) {
+    const int b = cr[i];
+    if (b >= 0 && b < nbe) {
+      last = i;
+      blk = b;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int ol = __shfl_xor(last, o), ob = __shfl_xor(blk, o);
+    if (ol > last) {
+      last = ol;
+      blk = ob;
+    }
+  }
+  if (lane == 0) a.row_end_out[r] = last < 0 ? 0 : last * bs + min(bs, e - (blk << bsh));
+}
+
+// GATHER: each query row walks its own candidate pool (NR = 1, one "sequence" per
+// row); otherwise the dense walk over whole sequences, NR = next_n rows each.
+template <int FMT, int HT, int NR, bool GATHER>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 1 ? 3 : 1))) void paged_logits_kernel(PagedArgs a) {
-  extern __shared__ int s_lds[];  // pref[B + 1], len[B]
+  extern __shared__ int s_lds[];  // pref[S + 1], len[S] (+ end[S] for the gather walk)
   __shared__ int s_scan[kThreads / 64];
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[FMT == 0 ? kThreads / 64 : 1][FMT == 0 ? kChunk * kTileStride : 16];
+  const int S = GATHER ? a.B * a.next_n : a.B;  // walks: sequences, or rows for the gather walk
   int *s_pref = s_lds;
-  int *s_len = s_lds + a.B + 1;
+  int *s_len = s_lds + S + 1;
+  int *s_end = s_lds + 2 * S + 1;
 
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);
@@ -129,18 +189,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
   const int g = lane >> 4;
   const int n = lane & 15;
   const int P = a.page_size;
-  const int cap = int(min(int64_t(a.width), int64_t(a.max_blocks) * P));
+  // dense: columns the row may reach; gather: positions the block table addresses
+  const int cap = GATHER ? int(min(int64_t(INT_MAX), int64_t(a.max_blocks) * P))
+                         : int(min(int64_t(a.width), int64_t(a.max_blocks) * P));
+  const int bsh = GATHER || a.block_max ? 31 - __builtin_clz(a.block_size) : 0;
 
   // ---- chunks per sequence, their prefix sum, sequence lengths (LDS) -------------
-  const int per = (a.B + kThreads - 1) / kThreads;
-  const int b_lo = min(a.B, tid * per), b_hi = min(a.B, b_lo + per);
+  const int per = (S + kThreads - 1) / kThreads;
+  const int b_lo = min(S, tid * per), b_hi = min(S, b_lo + per);
   int mine = 0;
   for (int b = b_lo; b < b_hi; ++b) {
-    int end[NR];
-    row_ends<NR>(a, b, cap, end);
     int len = 0;
+    if constexpr (GATHER) {
+      s_end[b] = gather_row_end(a, b, cap);
+      len = min(max(a.row_end_out[b], 0), a.width);  // pool length from the first pass
+    } else {
+      int end[NR];
+      row_ends<NR>(a, b, cap, end);
 #pragma unroll
-    for (int j = 0; j < NR; ++j) len = max(len, end[j]);
+      for (int j = 0; j < NR; ++j) len = max(len, end[j]);
+    }
     s_len[b] = len;
     mine += (len + kChunk - 1) / kChunk;
   }
@@ -150,8 +218,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
     s_pref[b] = run;
     run += (s_len[b] + kChunk - 1) / kChunk;
   }
-  if (tid == 0) s_pref[a.B] = total;
-  if (blockIdx.x == 0 && a.row_end_out) {
+  if (tid == 0) s_pref[S] = total;
+  if (!GATHER && blockIdx.x == 0 && a.row_end_out) {
     for (int r = tid; r < a.B * NR; r += kThreads) {
       int end[NR];
       row_ends<NR>(a, r / NR, cap, end);
@@ -185,7 +253,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
   // after a chunk's K loads are issued: memory operations complete in issue order, so
   // stores issued ahead of the block-table and K loads would delay them.
   const int fill_nu = (a.width + 255) / 256;
-  const int64_t fill_total = int64_t(a.B) * NR * fill_nu;
+  const int64_t fill_total = int64_t(S) * NR * fill_nu;
   int64_t fill_next = v;  // next unit of this wave
   auto fill_some = [&](int units) {
     for (int i = 0; i < units && fill_next < fill_total; ++i, fill_next += V) {
@@ -205,16 +273,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
   };
 
   // block-table entries of chunks [base, base + 16): lane l holds chunk base + l/4,
-  // 16-key group l%4 (0 past the wave's share or the sequence's end)
-  auto load_pages = [&](int base) -> int {
+  // 16-key group l%4 (0 past the wave's share or the sequence's end). The gather walk
+  // first reads the group's candidate block, and returns in `pos` the position of the
+  // group's first key (-1 when the group names no key below the row's end).
+  auto load_pages = [&](int base, int &pos) -> int {
     const int u = base + (lane >> 2);
     int pg = 0;
+    pos = -1;
     if (u < u1) {
-      const int bb = find_seq(s_pref, a.B, u);
+      const int bb = find_seq(s_pref, S, u);
       const int s = (u - s_pref[bb]) * kChunk + (lane & 3) * 16;
       if (s < s_len[bb]) {
-        const int pi = a.page_shift >= 0 ? s >> a.page_shift : s / P;
-        pg = min(max(a.block_table[int64_t(bb) * a.block_table_stride + pi], 0), a.num_pages - 1);
+        if constexpr (GATHER) {
+          const int e = s_end[bb];
+          const int blk = a.cand[int64_t(bb / a.row_repeat) * a.cand_row_stride + (s >> bsh)];
+          if (blk >= 0 && blk < (e >> bsh) + ((e & (a.block_size - 1)) != 0)) {
+            const int p = (blk << bsh) + (s & (a.block_size - 1));
+            if (p < e) {
+              pos = p;
+              const int pi = a.page_shift >= 0 ? p >> a.page_shift : p / P;
+              pg = min(max(a.block_table[int64_t(bb / a.next_n) * a.block_table_stride + pi], 0), a.num_pages - 1);
+            }
+          }
+        } else {
+          const int pi = a.page_shift >= 0 ? s >> a.page_shift : s / P;
+          pg = min(max(a.block_table[int64_t(bb) * a.block_table_stride + pi], 0), a.num_pages - 1);
+        }
       }
     }
     return pg;
@@ -222,7 +306,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
 
   // issue the loads of chunk `c` (index within sequence `b`) whose pages sit in lanes
   // 4*slot .. 4*slot+3 of `pg`
-  auto issue = [&](Chunk<FMT> &ch, int pg, int slot, int b, int c) {
+  auto issue = [&](Chunk<FMT> &ch, int pg, int pp, int slot, int b, int c) {
     const int key0 = c * kChunk;
     const int len = s_len[b];
     if constexpr (FMT == 0) ch.ksc = 0.f;
@@ -236,10 +320,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
         ch.kb[kg] = zero8();
         ch.ksb[kg] = 127;
       }
-      if (s < len) {
+      int kpos = s;  // position of the group's first key
+      if constexpr (GATHER) {
+        kpos = s < len ? __builtin_amdgcn_readlane(pp, 4 * slot + kg) : -1;
+        ch.gpos[kg] = kpos;
+      }
+      if (GATHER ? kpos >= 0 : s < len) {
         const int page = __builtin_amdgcn_readlane(pg, 4 * slot + kg);
         const uint8_t *pb = a.base + int64_t(page) * a.page_stride;
-        const int e0 = a.page_shift >= 0 ? s & (P - 1) : s % P;
+        const int e0 = a.page_shift >= 0 ? kpos & (P - 1) : kpos % P;
         if constexpr (FMT == 0) {
           const uint8_t *p = pb + (e0 + (lane >> 3)) * 128 + (lane & 7) * 16;
           ch.raw[2 * kg] = load16(p);
@@ -260,7 +349,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
   int qs[NR][HT];
   int end[NR];
   auto load_queries = [&](int b) {
-    row_ends<NR>(a, b, cap, end);
+    if constexpr (GATHER)
+      end[0] = s_end[b];
+    else
+      row_ends<NR>(a, b, cap, end);
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
       const int64_t r = int64_t(b) * NR + j;
@@ -329,13 +421,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
     }
     float res[NR];
 #pragma unroll
-    for (int j = 0; j < NR; ++j) res[j] = transpose_reduce4(part[j]);
+    for (int j = 0; j < NR; ++j) {
+      float val = transpose_reduce4(part[j]);
+      if constexpr (FMT == 0) val *= ch.ksc;
+      if constexpr (GATHER) {
+        // lane L holds key L = 16 g + n of the chunk, at position gpos[g] + n
+        int gp = ch.gpos[0];
+        if (g == 1) gp = ch.gpos[1];
+        if (g == 2) gp = ch.gpos[2];
+        if (g == 3) gp = ch.gpos[3];
+        res[j] = gp >= 0 && gp + n < end[j] ? val : ninf;
+      } else {
+        res[j] = col < end[j] ? val : ninf;
+      }
+    }
     if (col < a.width) {
 #pragma unroll
-      for (int j = 0; j < NR; ++j) {
-        float val = res[j];
-        if constexpr (FMT == 0) val *= ch.ksc;
-        a.logits[(int64_t(b) * NR + j) * a.logits_row_stride + col] = col < end[j] ? val : ninf;
+      for (int j = 0; j < NR; ++j) a.logits[(int64_t(b) * NR + j) * a.logits_row_stride + col] = res[j];
+    }
+    if constexpr (!GATHER) {
+      if (a.block_max) {
+        // the chunk holds whole blocks (block_size divides 64): one store per block
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+          float m = res[j];
+          for (int o = 1; o < a.block_size; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+          if ((lane & (a.block_size - 1)) == 0 && col < a.width)
+            a.block_max[(int64_t(b) * NR + j) * a.block_max_row_stride + (col >> bsh)] = m;
+        }
       }
     }
   };
@@ -346,8 +459,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
   auto stream = [&](const int u0, const int u1) {
     if (u0 >= u1) return;
     int pg_base = u0;
-    int pg = load_pages(pg_base);
-    int ib = find_seq(s_pref, a.B, u0);  // coordinates of the next chunk to issue
+    int pp = -1;
+    int pg = load_pages(pg_base, pp);
+    int ib = find_seq(s_pref, S, u0);  // coordinates of the next chunk to issue
     int ic = u0 - s_pref[ib];
     int iu = u0;
     constexpr int kRing = ring_depth<FMT, NR>();
@@ -356,13 +470,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
     auto issue_next = [&](Chunk<FMT> &slot_buf, int &slot_b, int &slot_c) {
       if (iu - pg_base >= 16) {
         pg_base = iu;
-        pg = load_pages(pg_base);
+        pg = load_pages(pg_base, pp);
       }
-      issue(slot_buf, pg, iu - pg_base, ib, ic);
+      issue(slot_buf, pg, pp, iu - pg_base, ib, ic);
       slot_b = ib;
       slot_c = ic;
       if (++iu < u1 && ++ic >= s_pref[ib + 1] - s_pref[ib]) {
-        ib = find_seq(s_pref, a.B, s_pref[ib + 1]);
+        ib = find_seq(s_pref, S, s_pref[ib + 1]);
         ic = 0;
       }
     };
@@ -386,11 +500,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
   };
   stream(u0, u1);
   fill_some(INT_MAX);
+  if constexpr (!GATHER) {
+    if (a.block_max) {
+      // blocks past each sequence's last chunk
+      const int nbm = (a.width + a.block_size - 1) >> bsh;
+      for (int r = v; r < S * NR; r += V) {
+        const int bb = r / NR;
+        const int j0 = ((s_pref[bb + 1] - s_pref[bb]) * kChunk) >> bsh;
+        for (int jb = j0 + lane; jb < nbm; jb += 64) a.block_max[int64_t(r) * a.block_max_row_stride + jb] = ninf;
+      }
+    }
+  }
 }
 
 // Persistent grid: as many workgroups as can be resident at once (a multiple of 8,
 // one equal slice per XCD), so every share starts immediately.
-template <int FMT, int HT, int NR>
+template <int FMT, int HT, int NR, bool GATHER>
 hipError_t launch_one(const PagedArgs &a, int num_cus, size_t lds, hipStream_t stream) {
   // resident workgroups per CU for this kernel and LDS size, looked up once per size
   static std::mutex mu;
@@ -401,24 +526,25 @@ hipError_t launch_one(const PagedArgs &a, int num_cus, size_t lds, hipStream_t s
     std::lock_guard<std::mutex> lock(mu);
     if (cached_lds != lds) {
       const hipError_t e =
-          hipOccupancyMaxActiveBlocksPerMultiprocessor(&cached, paged_logits_kernel<FMT, HT, NR>, kThreads, lds);
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&cached, paged_logits_kernel<FMT, HT, NR, GATHER>, kThreads, lds);
       if (e != hipSuccess) return e;
       cached_lds = lds;
     }
     per_cu = cached;
   }
   const int nwg = max(8, (max(per_cu, 1) * num_cus) / 8 * 8);
-  paged_logits_kernel<FMT, HT, NR><<<dim3(nwg), kThreads, lds, stream>>>(a);
+  paged_logits_kernel<FMT, HT, NR, GATHER><<<dim3(nwg), kThreads, lds, stream>>>(a);
   return hipGetLastError();
 }
 
 template <int FMT, int HT>
 hipError_t launch_nr(const PagedArgs &a, int num_cus, size_t lds, hipStream_t stream) {
+  if (a.cand) return launch_one<FMT, HT, 1, true>(a, num_cus, lds, stream);
   switch (a.next_n) {
-    case 1: return launch_one<FMT, HT, 1>(a, num_cus, lds, stream);
-    case 2: return launch_one<FMT, HT, 2>(a, num_cus, lds, stream);
-    case 3: return launch_one<FMT, HT, 3>(a, num_cus, lds, stream);
-    default: return launch_one<FMT, HT, 4>(a, num_cus, lds, stream);
+    case 1: return launch_one<FMT, HT, 1, false>(a, num_cus, lds, stream);
+    case 2: return launch_one<FMT, HT, 2, false>(a, num_cus, lds, stream);
+    case 3: return launch_one<FMT, HT, 3, false>(a, num_cus, lds, stream);
+    default: return launch_one<FMT, HT, 4, false>(a, num_cus, lds, stream);
   }
 }
 
@@ -434,7 +560,13 @@ hipError_t launch_fmt(const PagedArgs &a, int num_cus, size_t lds, hipStream_t s
 }  // namespace
 
 hipError_t launch_paged_logits(const PagedArgs &a, int num_cus, hipStream_t stream) {
-  const size_t lds = size_t(2 * a.B + 1) * sizeof(int);
+  if (a.cand) {
+    // the gather walk reads each row's pool length from row_end_out
+    pool_length_kernel<<<dim3(a.B * a.next_n), 64, 0, stream>>>(a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const size_t lds = a.cand ? size_t(3 * a.B * a.next_n + 1) * sizeof(int) : size_t(2 * a.B + 1) * sizeof(int);
   return a.fmt == 0 ? launch_fmt<0>(a, num_cus, lds, stream) : launch_fmt<1>(a, num_cus, lds, stream);
 }
 

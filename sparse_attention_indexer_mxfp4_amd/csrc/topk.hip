@@ -304,7 +304,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
   const int start = a.row_start ? min(max(a.row_start[row], 0), a.width) : 0;
-  const int end = min(max(a.row_end[row], 0), a.width);
+  const int e_in = max(a.row_end[row], 0);
+  const int end = min(a.end_div == 1 ? e_in : e_in / a.end_div + (e_in % a.end_div != 0), a.width);
   const int n = max(end - start, 0);
   const int k = a.k;
   int32_t *out = a.out + int64_t(row) * a.out_row_stride;

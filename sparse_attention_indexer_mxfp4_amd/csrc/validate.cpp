@@ -190,4 +190,67 @@ idx_status check_topk_to_slots(const void *topk, int64_t topk_row_stride, int32_
   return IDX_OK;
 }
 
+namespace {
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+}  // namespace
+
+idx_status check_block_max(const void *block_max, int64_t block_max_row_stride, int32_t block_size, int32_t width) {
+  if (block_size != 16 && block_size != 32 && block_size != 64) return IDX_ERR_SHAPE;
+  if (!block_max) return IDX_ERR_NULL;
+  if (block_max_row_stride < (int64_t(width) + block_size - 1) / block_size || !aligned(block_max, 4))
+    return IDX_ERR_STRIDE;
+  return IDX_OK;
+}
+
+idx_status check_candidate_list(const void *cand, int64_t cand_row_stride, int32_t n_cand, int32_t block_size,
+                                int32_t row_repeat) {
+  if (n_cand < 1 || !pow2(block_size) || row_repeat < 1) return IDX_ERR_SHAPE;
+  if (int64_t(n_cand) * block_size > INT32_MAX) return IDX_ERR_SHAPE;
+  if (!cand) return IDX_ERR_NULL;
+  if (cand_row_stride < n_cand || !aligned(cand, 4)) return IDX_ERR_STRIDE;
+  return IDX_OK;
+}
+
+idx_status check_gather(int32_t B, int32_t next_n, int32_t block_size, const void *pool_logits,
+                        int64_t pool_row_stride, int32_t n_cand, const void *pool_end_out) {
+  // the per-row walk keeps three ints per row in LDS; chunk offsets stay in int32
+  if (B < 0 || next_n < 1 || int64_t(B) * next_n > kMaxBatch) return IDX_ERR_SHAPE;
+  if (int64_t(B) * next_n * ((int64_t(n_cand) * block_size + 63) / 64) > INT32_MAX) return IDX_ERR_SHAPE;
+  // a 16-key group of the walk lies inside one pool block and one page
+  if (block_size < 16 || block_size > (1 << 20)) return IDX_ERR_SHAPE;
+  if (B > 0 && (!pool_logits || !pool_end_out)) return IDX_ERR_NULL;
+  if (B > 0 && !aligned(pool_end_out, 4)) return IDX_ERR_STRIDE;
+  const int64_t width = int64_t(n_cand) * block_size;
+  if (B > 0 && (pool_row_stride < width || pool_row_stride % 4 || !aligned(pool_logits, 16))) return IDX_ERR_STRIDE;
+  return IDX_OK;
+}
+
+idx_status check_candidate_mask(const void *logits, int64_t logits_row_stride, int32_t rows, int32_t width,
+                                const void *row_end, int32_t block_size, bool *empty) {
+  *empty = false;
+  if (rows < 0 || width < 0 || !pow2(block_size)) return IDX_ERR_SHAPE;
+  // one LDS byte per block of the row
+  if ((int64_t(width) + block_size - 1) / block_size >= 65536) return IDX_ERR_SHAPE;
+  if (rows == 0 || width == 0) {
+    *empty = true;
+    return IDX_OK;
+  }
+  if (!logits || !row_end) return IDX_ERR_NULL;
+  if (logits_row_stride < width || logits_row_stride % 4 || !aligned(logits, 16) || !aligned(row_end, 4))
+    return IDX_ERR_STRIDE;
+  return IDX_OK;
+}
+
+idx_status check_remap(const void *topk, int64_t topk_row_stride, int32_t rows, int32_t k, bool *empty) {
+  *empty = false;
+  if (rows < 0 || k < 0) return IDX_ERR_SHAPE;
+  if (rows == 0 || k == 0) {
+    *empty = true;
+    return IDX_OK;
+  }
+  if (!topk) return IDX_ERR_NULL;
+  if (topk_row_stride < k || !aligned(topk, 4)) return IDX_ERR_STRIDE;
+  return IDX_OK;
+}
+
 }  // namespace idx

@@ -60,4 +60,14 @@ idx_status check_topk_to_slots(const void *topk, int64_t topk_row_stride, int32_
                                int64_t block_table_stride, int32_t max_blocks, int32_t page_size,
                                const void *slots_out, const void *indptr_out, bool *empty);
 
+// two-level indexer
+idx_status check_block_max(const void *block_max, int64_t block_max_row_stride, int32_t block_size, int32_t width);
+idx_status check_candidate_list(const void *cand, int64_t cand_row_stride, int32_t n_cand, int32_t block_size,
+                                int32_t row_repeat);
+idx_status check_gather(int32_t B, int32_t next_n, int32_t block_size, const void *pool_logits,
+                        int64_t pool_row_stride, int32_t n_cand, const void *pool_end_out);
+idx_status check_candidate_mask(const void *logits, int64_t logits_row_stride, int32_t rows, int32_t width,
+                                const void *row_end, int32_t block_size, bool *empty);
+idx_status check_remap(const void *topk, int64_t topk_row_stride, int32_t rows, int32_t k, bool *empty);
+
 }  // namespace idx

@@ -74,14 +74,7 @@ def idx_mqa_logits(q: torch.Tensor, k: torch.Tensor, k_scale: torch.Tensor, w: t
     return logits
 
 
-def idx_paged_mqa_logits(pool: torch.Tensor, fmt: int, page_size: int, q: torch.Tensor, q_scale: torch.Tensor | None,
-                         w: torch.Tensor, context_lens: torch.Tensor, block_table: torch.Tensor, width: int,
-                         ctx_per_row: bool = False, logits: torch.Tensor | None = None,
-                         row_end_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
-    """Paged decode / MTP logits. q [B, next_n, H, 128] (fp8) or [B, next_n, H, 64] (MXFP4) uint8,
-    q_scale [B, next_n, H] int32 (MXFP4) or None, w [B*next_n, H] f32, context_lens [B] (or
-    [B*next_n] with ctx_per_row) int32, block_table [B, max_blocks] int32.
-    Returns (logits [B*next_n, width] f32, row_end [B*next_n] int32)."""
+def _paged_inputs(pool, fmt, page_size, q, q_scale, w, context_lens, block_table):
     cache = paged_cache(pool, fmt, page_size)
     _need(q, torch.uint8, "q"); _need(w, torch.float32, "w"); _need(context_lens, torch.int32, "context_lens")
     _need(block_table, torch.int32, "block_table")
@@ -90,22 +83,129 @@ def idx_paged_mqa_logits(pool: torch.Tensor, fmt: int, page_size: int, q: torch.
         _need(q_scale, torch.int32, "q_scale"); _contig(q_scale, "q_scale")
     if block_table.stride(1) != 1:
         raise ValueError("block_table rows must be dense")
+    return cache
+
+
+def idx_paged_mqa_logits(pool: torch.Tensor, fmt: int, page_size: int, q: torch.Tensor, q_scale: torch.Tensor | None,
+                         w: torch.Tensor, context_lens: torch.Tensor, block_table: torch.Tensor, width: int,
+                         ctx_per_row: bool = False, logits: torch.Tensor | None = None,
+                         row_end_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Paged decode / MTP logits. q [B, next_n, H, 128] (fp8) or [B, next_n, H, 64] (MXFP4) uint8,
+    q_scale [B, next_n, H] int32 (MXFP4) or None, w [B*next_n, H] f32, context_lens [B] (or
+    [B*next_n] with ctx_per_row) int32, block_table [B, max_blocks] int32.
+    Returns (logits [B*next_n, width] f32, row_end [B*next_n] int32)."""
+    logits, row_end_out, _ = idx_paged_mqa_logits_block_max(
+        pool, fmt, page_size, q, q_scale, w, context_lens, block_table, width, 0, ctx_per_row, logits, row_end_out,
+        None, workspace)
+    return logits, row_end_out
+
+
+def idx_paged_mqa_logits_block_max(pool: torch.Tensor, fmt: int, page_size: int, q: torch.Tensor,
+                                   q_scale: torch.Tensor | None, w: torch.Tensor, context_lens: torch.Tensor,
+                                   block_table: torch.Tensor, width: int, block_size: int, ctx_per_row: bool = False,
+                                   logits: torch.Tensor | None = None, row_end_out: torch.Tensor | None = None,
+                                   block_max: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """idx_paged_mqa_logits that also returns the block maxima [B*next_n, ceil(width /
+    block_size)] f32 (block_size 16, 32 or 64; 0: none, block_max is None).
+    Returns (logits, row_end, block_max)."""
+    cache = _paged_inputs(pool, fmt, page_size, q, q_scale, w, context_lens, block_table)
     B, next_n, H = q.shape[:3]
     rows = B * next_n
     if logits is None:
         logits = torch.empty((rows, (width + 3) // 4 * 4), dtype=torch.float32, device=q.device)[:, :width]
     if row_end_out is None:
         row_end_out = torch.empty(rows, dtype=torch.int32, device=q.device)
+    if block_size and block_max is None:
+        block_max = torch.empty((rows, -(-width // block_size)), dtype=torch.float32, device=q.device)
+    if block_max is not None:
+        _need(block_max, torch.float32, "block_max")
+        if block_max.stride(1) != 1:
+            raise ValueError("block_max rows must be dense")
     lib = _abi.lib()
     need = lib.idx_paged_mqa_logits_workspace(B, next_n, H, ctypes.byref(cache))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _abi.check(lib.idx_paged_mqa_logits(
+    _abi.check(lib.idx_paged_mqa_logits_block_max(
         ctypes.byref(cache), _ptr(q), _ptr(q_scale), _ptr(w), _ptr(context_lens), int(ctx_per_row),
         _ptr(block_table), block_table.stride(0), block_table.shape[1], B, next_n, H, _ptr(logits),
-        logits.stride(0), width, _ptr(row_end_out), _ptr(workspace), ws_bytes, _stream()))
-    return logits, row_end_out
+        logits.stride(0), width, _ptr(row_end_out), _ptr(block_max) if block_size else None,
+        block_max.stride(0) if block_size else 0, block_size, _ptr(workspace), ws_bytes, _stream()))
+    return logits, row_end_out, block_max if block_size else None
+
+
+def _cand_rows(cand: torch.Tensor) -> None:
+    _need(cand, torch.int32, "cand")
+    if cand.dim() != 2 or cand.stride(1) != 1:
+        raise ValueError("cand must be 2-D with dense rows")
+
+
+def idx_candidate_blocks(block_max: torch.Tensor, row_end: torch.Tensor, block_size: int, n_cand: int,
+                         out: torch.Tensor | None = None) -> torch.Tensor:
+    """The candidate pool: per row, the n_cand best blocks of block_max [rows, num_blocks]
+    f32 within ceil(row_end / block_size), ascending, -1 padded -> [rows, n_cand] int32."""
+    _need(block_max, torch.float32, "block_max"); _need(row_end, torch.int32, "row_end")
+    _contig(row_end, "row_end")
+    if block_max.stride(1) != 1:
+        raise ValueError("block_max rows must be dense")
+    rows, nb = block_max.shape
+    if out is None:
+        out = torch.empty((rows, n_cand), dtype=torch.int32, device=block_max.device)
+    lib = _abi.lib()
+    need = lib.idx_topk_workspace(rows, nb, n_cand)
+    workspace = torch.empty(need, dtype=torch.uint8, device=block_max.device) if need else None
+    _abi.check(lib.idx_candidate_blocks(_ptr(block_max), block_max.stride(0), rows, nb, _ptr(row_end), block_size,
+                                        n_cand, _ptr(out), out.stride(0), _ptr(workspace), need, _stream()))
+    return out
+
+
+def idx_apply_candidate_mask(logits: torch.Tensor, row_end: torch.Tensor, cand: torch.Tensor, block_size: int,
+                             row_repeat: int = 1) -> torch.Tensor:
+    """In place: columns below row_end outside the row's candidate blocks become -inf."""
+    _need(logits, torch.float32, "logits"); _need(row_end, torch.int32, "row_end")
+    _contig(row_end, "row_end"); _cand_rows(cand)
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be dense")
+    rows, width = logits.shape
+    _abi.check(_abi.lib().idx_apply_candidate_mask(_ptr(logits), logits.stride(0), rows, width, _ptr(row_end),
+                                                   _ptr(cand), cand.stride(0), cand.shape[1], block_size,
+                                                   row_repeat, _stream()))
+    return logits
+
+
+def idx_paged_mqa_logits_gather(pool: torch.Tensor, fmt: int, page_size: int, q: torch.Tensor,
+                                q_scale: torch.Tensor | None, w: torch.Tensor, context_lens: torch.Tensor,
+                                block_table: torch.Tensor, cand: torch.Tensor, block_size: int, row_repeat: int = 1,
+                                ctx_per_row: bool = False, pool_logits: torch.Tensor | None = None,
+                                pool_end: torch.Tensor | None = None):
+    """Score only each row's candidate pool (cand [rows / row_repeat, n_cand] int32).
+    Returns (pool_logits [B*next_n, n_cand*block_size] f32, pool_end [B*next_n] int32)."""
+    cache = _paged_inputs(pool, fmt, page_size, q, q_scale, w, context_lens, block_table)
+    _cand_rows(cand)
+    B, next_n, H = q.shape[:3]
+    rows = B * next_n
+    width = cand.shape[1] * block_size
+    if pool_logits is None:
+        pool_logits = torch.empty((rows, (width + 3) // 4 * 4), dtype=torch.float32, device=q.device)[:, :width]
+    if pool_end is None:
+        pool_end = torch.empty(rows, dtype=torch.int32, device=q.device)
+    _abi.check(_abi.lib().idx_paged_mqa_logits_gather(
+        ctypes.byref(cache), _ptr(q), _ptr(q_scale), _ptr(w), _ptr(context_lens), int(ctx_per_row),
+        _ptr(block_table), block_table.stride(0), block_table.shape[1], B, next_n, H, _ptr(cand), cand.stride(0),
+        cand.shape[1], block_size, row_repeat, _ptr(pool_logits), pool_logits.stride(0), _ptr(pool_end),
+        _stream()))
+    return pool_logits, pool_end
+
+
+def idx_remap_compact_topk(topk: torch.Tensor, cand: torch.Tensor, block_size: int, row_repeat: int = 1):
+    """In place: top-k entries over pool slots -> positions (see include/idx.h)."""
+    _need(topk, torch.int32, "topk"); _cand_rows(cand)
+    if topk.dim() != 2 or topk.stride(1) != 1:
+        raise ValueError("topk must be 2-D with dense rows")
+    rows, k = topk.shape
+    _abi.check(_abi.lib().idx_remap_compact_topk(_ptr(topk), topk.stride(0), rows, k, _ptr(cand), cand.stride(0),
+                                                 cand.shape[1], block_size, row_repeat, _stream()))
+    return topk
 
 
 def idx_topk(logits: torch.Tensor, row_start: torch.Tensor | None, row_end: torch.Tensor, k: int,

@@ -204,6 +204,65 @@ def test_topk_to_slots_checks(lib):
     assert f(P, 8, -1, 8, None, 1, 2, None, P, 4, 4, 16, P, P, None, None) == SHAPE
 
 
+def test_two_level_checks(lib):
+    c = _cache()
+    bm = lib.idx_paged_mqa_logits_block_max
+
+    def _bm(**kw):
+        a = dict(bmp=P, bms=32, bs=16, B=4)
+        a.update(kw)
+        return bm(ctypes.byref(c), P, None, P, P, 0, P, 8, 8, a["B"], 1, 64, P, 512, 512, None, a["bmp"], a["bms"],
+                  a["bs"], None, 0, None)
+    assert _bm(bs=8) == SHAPE  # block maxima need 16, 32 or 64
+    assert _bm(bs=128) == SHAPE
+    assert _bm(bmp=None) == NULL
+    assert _bm(bms=31) == STRIDE  # 512 / 16 blocks per row
+    assert _bm(bmp=P + 2) == STRIDE
+    assert _bm(B=0) == OK
+    assert _bm(bs=0, bmp=None, B=0) == OK  # no block maxima asked for
+
+    g = lib.idx_paged_mqa_logits_gather
+
+    def _g(**kw):
+        a = dict(cand=P, cs=8, n=8, bs=64, rr=1, out=P, os=512, B=4, nn=1)
+        a.update(kw)
+        return g(ctypes.byref(c), P, None, P, P, 0, P, 8, 8, a["B"], a["nn"], 64, a["cand"], a["cs"], a["n"],
+                 a["bs"], a["rr"], a["out"], a["os"], a.get("ends", P), None)
+    assert _g(bs=8) == SHAPE  # a 16-key group must sit inside one pool block
+    assert _g(bs=48) == SHAPE  # not a power of two
+    assert _g(n=0) == SHAPE
+    assert _g(rr=0) == SHAPE
+    assert _g(B=4096, nn=4) == SHAPE  # rows kept in LDS
+    assert _g(cand=None) == NULL
+    assert _g(cs=7) == STRIDE
+    assert _g(os=510) == STRIDE  # the pool row is n * block = 512 wide
+    assert _g(out=None) == NULL
+    assert _g(ends=None) == NULL  # the pool lengths pass through it
+    assert _g(ends=P + 2) == STRIDE
+    assert _g(B=0) == OK
+
+    cb = lib.idx_candidate_blocks
+    assert cb(P, 32, 4, 32, P, 48, 8, P, 8, None, 0, None) == SHAPE  # block size a power of two
+    assert cb(P, 31, 4, 32, P, 16, 8, P, 8, None, 0, None) == STRIDE
+    assert cb(P, 32, 4, 32, None, 16, 8, P, 8, None, 0, None) == NULL
+    assert cb(P, 32, 0, 32, None, 16, 8, None, 8, None, 0, None) == OK
+
+    m = lib.idx_apply_candidate_mask
+    assert m(P, 512, 4, 512, P, P, 8, 8, 24, 1, None) == SHAPE
+    assert m(P, 512, 4, 2 ** 20, P, P, 8, 8, 1, 1, None) == SHAPE  # one LDS byte per block
+    assert m(P, 510, 4, 510, P, P, 8, 8, 16, 1, None) == STRIDE
+    assert m(P + 4, 512, 4, 512, P, P, 8, 8, 16, 1, None) == STRIDE
+    assert m(P, 512, 4, 512, P, None, 8, 8, 16, 1, None) == NULL
+    assert m(P, 512, 4, 512, P, P, 7, 8, 16, 1, None) == STRIDE
+    assert m(P, 512, 4, 512, P, P, 8, 8, 16, 0, None) == SHAPE
+
+    r = lib.idx_remap_compact_topk
+    assert r(P, 8, 4, 16, P, 8, 8, 16, 1, None) == STRIDE
+    assert r(None, 16, 4, 16, P, 8, 8, 16, 1, None) == NULL
+    assert r(P, 16, 4, 16, P, 8, 8, 12, 1, None) == SHAPE
+    assert r(P, 16, 0, 16, P, 8, 8, 16, 1, None) == OK
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path; a GPU is visible")
 def test_valid_call_without_device_reports_device_error(lib):
     # arguments pass every host check, so the call reaches the device query, which

@@ -137,5 +137,5 @@ def test_row_repeat_shares_a_candidate_row():
 
 def test_remap_keeps_pads():
     cand = np.array([[5, -1]])
-    t = np.array([[0, 3, 4, -1]])
-    np.testing.assert_array_equal(candidates.remap_compact_topk(t, cand, 4), [[20, 23, -1, -1]])
+    t = np.array([[0, 3, 4, -1, 8, 9]])  # slot 4 has candidate -1; slots 8 and 9 lie past the list
+    np.testing.assert_array_equal(candidates.remap_compact_topk(t, cand, 4), [[20, 23, -1, -1, -1, -1]])
