@@ -79,6 +79,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--two-level", action="store_true",
+                   help="time the two-level indexer on a paged workload instead: the source walk with block "
+                        "maxima, the candidate pool, and a consumer that scores only the pool (prints its own "
+                        "JSON line)")
+    p.add_argument("--pool-blocks", type=int, default=64, help="two-level: candidate blocks per row")
+    p.add_argument("--pool-block", type=int, default=64, help="two-level: keys per candidate block (16, 32, 64)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device copy (the reference kernel for scaling "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
@@ -241,6 +247,10 @@ def main():
         def topk_call():
             ops.idx_topk(logits, None, ends, wl.topk, out=out)
 
+        if args.two_level:
+            two_level(args, wl, ops, pools, copies, fmt, q, q_scale, w, ctx, bt, logits, ends, out, logits_call,
+                      topk_call)
+            return
         ends_host = None
     else:
         fmt = ops.FP8
@@ -357,6 +367,128 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, wl)
+    print(json.dumps(result), flush=True)
+
+
+def timed_graph(torch, fn, steps):
+    """Per-launch duration (ms) of fn(i), i < steps, captured back to back in one HIP graph:
+    one untimed replay, then one replay between two HIP events on the launch stream."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    g.replay()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / steps
+
+
+def two_level(args, wl, ops, pools, copies, fmt, q, q_scale, w, ctx, bt, logits, ends, out, logits_call, topk_call):
+    """The two-level indexer on one paged step: a source layer (the dense walk that also
+    writes block maxima, then the pool: each row's best blocks) and one consumer layer
+    that scores only the pool (gathered walk, top-k over the pool, remap to positions),
+    next to the same consumer run densely (logits + top-k over the whole context)."""
+    import torch
+
+    dev = q.device
+    block, n = args.pool_block, args.pool_blocks
+    rows = wl.rows
+    nb = -(-wl.width // block)
+    bm = torch.empty((rows, nb), dtype=torch.float32, device=dev)
+    cand = torch.empty((rows, n), dtype=torch.int32, device=dev)
+    pw = n * block
+    pool = torch.empty((rows, pw), dtype=torch.float32, device=dev)
+    pend = torch.empty(rows, dtype=torch.int32, device=dev)
+    pout = torch.empty((rows, wl.topk), dtype=torch.int32, device=dev)
+
+    def source(i):
+        ops.idx_paged_mqa_logits_block_max(pools[i % copies], fmt, wl.page_size, q, q_scale, w, ctx, bt, wl.width,
+                                           block, logits=logits, row_end_out=ends, block_max=bm)
+
+    def select(i):
+        ops.idx_candidate_blocks(bm, ends, block, n, out=cand)
+
+    def gather(i):
+        ops.idx_paged_mqa_logits_gather(pools[i % copies], fmt, wl.page_size, q, q_scale, w, ctx, bt, cand, block,
+                                        pool_logits=pool, pool_end=pend)
+
+    def pool_topk(i):
+        ops.idx_topk(pool, None, pend, wl.topk, out=pout)
+
+    def remap(i):
+        ops.idx_remap_compact_topk(pout, cand, block)
+
+    for i in range(args.warmup):
+        source(i); select(i); gather(i); pool_topk(i); remap(i)
+    torch.cuda.synchronize()
+    # algorithmic bytes of the gathered walk: each row reads the keys its pool names
+    # (once per row), its queries and weights, one candidate entry per block and one
+    # block-table entry per 16-key group; it writes the whole pool row
+    e = ends.cpu().numpy().astype(np.int64)
+    c = cand.cpu().numpy().astype(np.int64)
+    nbe = -(-e // block)
+    ok = (c >= 0) & (c < nbe[:, None])
+    keys_per_row = np.where(ok, np.minimum(block, e[:, None] - c * block), 0).sum(axis=1)
+    pool_keys = int(keys_per_row.sum())
+    D, H = wl.D, wl.H
+    per_key = D + 4 if wl.fmt == "fp8" else D // 2 + D // 32
+    per_q = D if wl.fmt == "fp8" else D // 2 + 4
+    gbytes = (pool_keys * per_key + rows * H * (per_q + 4) + rows * n * 4 + int(np.ceil(keys_per_row / 16).sum()) * 4
+              + rows * 8 + rows * pw * 4)
+    dense_keys, _, _ = paged_work(wl, e)
+
+    t = {name: timed_graph(torch, fn, args.steps) for name, fn in
+         (("dense_logits", logits_call), ("dense_topk", lambda i: topk_call()), ("source", source),
+          ("select", select), ("gather", gather), ("pool_topk", pool_topk), ("remap", remap))}
+
+    def consumer(i):
+        gather(i); pool_topk(i); remap(i)
+
+    consumer_ms = timed_graph(torch, consumer, args.steps)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(args.steps):
+            source(i); select(i); consumer(i)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    achieved = gbytes / (t["gather"] * 1e-3) / 1e9
+    result = {
+        "metric": "two-level indexer consumer: pool keys scored/sec (gathered walk + top-k + remap), 1 MI355X",
+        "value": round(pool_keys / (consumer_ms * 1e-3), 1),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if wl.fmt == "fp8" else "fp4",
+        "data": "synthetic",
+        "config": {"workload": wl.name + f" two-level pool {n}x{block}", "pool_blocks": n, "pool_block": block,
+                   "topk": wl.topk, "pool_keys_per_step": pool_keys, "dense_keys_per_step": dense_keys,
+                   "timing": "step = source + pool + consumer, K steps in one HIP graph; per-kernel times from HIP "
+                             "events around a graph of K back-to-back launches of that call",
+                   "source_ms": round(t["source"], 4), "dense_logits_ms": round(t["dense_logits"], 4),
+                   "select_ms": round(t["select"], 4), "gather_ms": round(t["gather"], 4),
+                   "pool_topk_ms": round(t["pool_topk"], 4), "remap_ms": round(t["remap"], 4),
+                   "consumer_ms": round(consumer_ms, 4),
+                   "dense_consumer_ms": round(t["dense_logits"] + t["dense_topk"], 4), "k_cache_copies": copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("paged_logits_kernel", wl.name + f" two-level pool {n}x{block}"),
+                     "kernel": "paged_logits_kernel (gathered walk)", "kernel_ms": round(t["gather"], 4),
+                     "algorithmic_bytes": gbytes},
+    }
     print(json.dumps(result), flush=True)
 
 

@@ -57,6 +57,32 @@ __device__ __forceinline__ float transpose_reduce4(const float (&p)[4]) {
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
+// max of x over the 16 lanes of a DPP row (every lane receives it): rotations by
+// 8, 4, 2 and 1 lanes within the row
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));  // row_ror:8
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)));  // row_ror:4
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false)));  // row_ror:2
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false)));  // row_ror:1
+  return x;
+}
+
+// max of x over aligned groups of `group` lanes (16, 32 or 64); every lane receives
+// its group's. Past a row, a swap with itself hands each lane its neighbouring row
+// (permlane16) or half (permlane32).
+__device__ __forceinline__ float group_max(float x, int group) {
+  x = row16_max(x);
+  if (group >= 32) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  }
+  if (group >= 64) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  }
+  return x;
+}
+
 // 4x4 transpose across the four 16-lane groups: on return r[i] in lane group g holds
 // what r[g] held in lane group i (same lane within the group). Two permlane32 swaps
 // then two permlane16 swaps, no arithmetic.

@@ -41,7 +41,7 @@
 // Two-level indexer (page "vllm.v1.attention.ops.rocm_paged_mxfp4_indexer", module
 // description and rocm_mxfp4_sparse_mqa_indexer):
 //   - block maxima: the candidate source's walk also reduces each chunk's stored
-//     logits to the maxima of its 16-, 32- or 64-key blocks (lane shuffles) and
+//     logits to the maxima of its 16-, 32- or 64-key blocks (DPP and permlane swaps) and
 //     stores one value per block; blocks past a sequence's chunks get -inf with the
 //     tail;
 //   - gather walk: a consumer row scores only its candidate pool. Each query row is
@@ -444,8 +444,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
         // the chunk holds whole blocks (block_size divides 64): one store per block
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
-          float m = res[j];
-          for (int o = 1; o < a.block_size; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+          const float m = group_max(res[j], a.block_size);
           if ((lane & (a.block_size - 1)) == 0 && col < a.width)
             a.block_max[(int64_t(b) * NR + j) * a.block_max_row_stride + (col >> bsh)] = m;
         }
