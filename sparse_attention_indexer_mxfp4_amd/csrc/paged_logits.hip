@@ -117,19 +117,21 @@ __device__ __forceinline__ void row_ends(const PagedArgs &a, int b, int cap, int
 // LDS tile at scoring time. MXFP4: kb[kg] is already the B operand of key group kg.
 template <int FMT>
 struct Chunk;
-// The gather walk also keeps, per 16-key group, the position of its first key (-1 for
-// a group that names no key of the row).
+// The gather walk also keeps, in lane L, the position of the first key of L's own
+// 16-key group (group L / 16; -1 for a group that names no key of the row). A per-lane
+// value rather than four per-group ones picked by lane: a pick indexed by lane would
+// leave the ring in scratch memory.
 template <>
 struct Chunk<0> {
   v4i raw[8];
   float ksc;
-  int gpos[4];
+  int lpos;
 };
 template <>
 struct Chunk<1> {
   v8i kb[4];
   int ksb[4];
-  int gpos[4];
+  int lpos;
 };
 
 // Gather walk: the row's own end (exclusive), as for the dense walk
@@ -310,6 +312,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
     const int key0 = c * kChunk;
     const int len = s_len[b];
     if constexpr (FMT == 0) ch.ksc = 0.f;
+    if constexpr (GATHER) ch.lpos = -1;
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg) {
       const int s = key0 + kg * 16;  // 16 | P keeps a group inside one page
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
       int kpos = s;  // position of the group's first key
       if constexpr (GATHER) {
         kpos = s < len ? __builtin_amdgcn_readlane(pp, 4 * slot + kg) : -1;
-        ch.gpos[kg] = kpos;
+        if (g == kg) ch.lpos = kpos;
       }
       if (GATHER ? kpos >= 0 : s < len) {
         const int page = __builtin_amdgcn_readlane(pg, 4 * slot + kg);
@@ -425,12 +428,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
       float val = transpose_reduce4(part[j]);
       if constexpr (FMT == 0) val *= ch.ksc;
       if constexpr (GATHER) {
-        // lane L holds key L = 16 g + n of the chunk, at position gpos[g] + n
-        int gp = ch.gpos[0];
-        if (g == 1) gp = ch.gpos[1];
-        if (g == 2) gp = ch.gpos[2];
-        if (g == 3) gp = ch.gpos[3];
-        res[j] = gp >= 0 && gp + n < end[j] ? val : ninf;
+        // lane L holds key L = 16 g + n of the chunk, at position lpos + n
+        res[j] = ch.lpos >= 0 && ch.lpos + n < end[j] ? val : ninf;
       } else {
         res[j] = col < end[j] ? val : ninf;
       }
