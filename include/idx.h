@@ -297,6 +297,30 @@ idx_status idx_topk_to_slots(const int32_t *topk, int64_t topk_row_stride, int32
                              hipStream_t stream);
 
 /*
+ * idx_paged_prefill_logits - a prefill chunk straight off the paged cache: M query rows
+ * of one sequence, row r scoring keys [0, row_end[r]) of that sequence through its
+ * block-table row, with no gather of K. Page "vllm.v1.attention.ops.rocm_paged_mxfp4_indexer",
+ * module description (the kernel reads the paged K cache in place, prefill included)
+ * and rocm_mxfp4_sparse_attn_indexer (prefill chunks walk the same cache as decode).
+ * Every row's logit of key s is computed exactly as idx_paged_mqa_logits computes it.
+ *
+ *   cache         the paged K cache (fp8 or MXFP4), as idx_paged_mqa_logits.
+ *   q             [M, H, D] e4m3 (fp8) or [M, H, D/2] packed e2m1 (MXFP4), 16-byte aligned.
+ *   q_scale       MXFP4: [M, H] int32 (4 e8m0 bytes, as idx_q_quant); fp8: NULL.
+ *   w             [M, H] fp32.
+ *   row_end       [M] int32: row r's causal end (e.g. position + 1, or the compressed
+ *                 count), clamped to [0, min(width, max_blocks * page_size)].
+ *   block_table   [max_blocks] int32: the sequence's pages.
+ *   logits        [M, width] fp32 with logits_row_stride (multiple of 4, 16-byte
+ *                 aligned); -inf at and past each row's end.
+ *   Limits: M >= 0; M * ceil(width / 64) < 2^31; rows are walked two at a time.
+ */
+idx_status idx_paged_prefill_logits(const idx_paged_cache *cache, const void *q, const int32_t *q_scale,
+                                    const float *w, const int32_t *row_end, const int32_t *block_table,
+                                    int32_t max_blocks, int32_t M, int32_t H, float *logits,
+                                    int64_t logits_row_stride, int32_t width, hipStream_t stream);
+
+/*
  * Two-level indexer. Page "vllm.v1.attention.ops.rocm_paged_mxfp4_indexer": a candidate
  * source layer takes block maxima from the same walk that writes its logits
  * (rocm_mxfp4_sparse_attn_indexer with candidate_write; block scores sized

@@ -168,6 +168,41 @@ idx_status idx_paged_mqa_logits_gather(const idx_paged_cache *cache, const void 
   return launched(idx::launch_paged_logits(a, cus, stream));
 }
 
+idx_status idx_paged_prefill_logits(const idx_paged_cache *cache, const void *q, const int32_t *q_scale,
+                                    const float *w, const int32_t *row_end, const int32_t *block_table,
+                                    int32_t max_blocks, int32_t M, int32_t H, float *logits,
+                                    int64_t logits_row_stride, int32_t width, hipStream_t stream) {
+  // pairs of consecutive rows share one walk over the sequence's pages (two rows per
+  // walk keep two waves per SIMD; measured on the 8192 x 8192 MXFP4 chunk: 524 us
+  // against 650 us for one row and 783 us for four); an odd last row walks alone
+  constexpr int32_t kWalkRows = 2;
+  if (M < 0) return IDX_ERR_SHAPE;
+  const int32_t groups = M / kWalkRows, tail = M % kWalkRows;
+  bool empty = false;
+  idx_status s = idx::check_paged_mqa_logits(cache, q, q_scale, w, row_end, block_table, max_blocks, max_blocks,
+                                             groups + tail, 1, H, logits, logits_row_stride, width, nullptr, 0,
+                                             &empty);
+  if (s != IDX_OK || empty) return s;
+  if (int64_t(M) * ((int64_t(width) + 63) / 64) > INT32_MAX) return IDX_ERR_SHAPE;
+  int cus = 0;
+  if ((s = current_device(&cus)) != IDX_OK) return s;
+  const int64_t qrow = int64_t(H) * (cache->fmt == IDX_KV_FP8_E4M3 ? cache->head_dim : cache->head_dim / 2);
+  if (groups > 0) {
+    idx::PagedArgs a = paged_args(cache, q, q_scale, w, row_end, 1, block_table, 0, max_blocks, groups, kWalkRows,
+                                  H, logits, logits_row_stride, width, nullptr);
+    if ((s = launched(idx::launch_paged_logits(a, cus, stream))) != IDX_OK) return s;
+  }
+  if (tail > 0) {
+    const int64_t r0 = int64_t(groups) * kWalkRows;
+    idx::PagedArgs a = paged_args(cache, static_cast<const uint8_t *>(q) + r0 * qrow,
+                                  q_scale ? q_scale + r0 * H : nullptr, w + r0 * H, row_end + r0, 1, block_table, 0,
+                                  max_blocks, tail, 1, H, logits + r0 * logits_row_stride, logits_row_stride, width,
+                                  nullptr);
+    if ((s = launched(idx::launch_paged_logits(a, cus, stream))) != IDX_OK) return s;
+  }
+  return IDX_OK;
+}
+
 idx_status idx_candidate_blocks(const float *block_max, int64_t block_max_row_stride, int32_t rows,
                                 int32_t num_blocks, const int32_t *row_end, int32_t block_size, int32_t n_cand,
                                 int32_t *cand_out, int64_t cand_row_stride, void *workspace,

@@ -134,6 +134,22 @@ def idx_paged_mqa_logits_block_max(pool: torch.Tensor, fmt: int, page_size: int,
     return logits, row_end_out, block_max if block_size else None
 
 
+def idx_paged_prefill_logits(pool: torch.Tensor, fmt: int, page_size: int, q: torch.Tensor,
+                             q_scale: torch.Tensor | None, w: torch.Tensor, row_end: torch.Tensor,
+                             block_table_row: torch.Tensor, width: int, logits: torch.Tensor | None = None):
+    """A prefill chunk of one sequence off the paged cache: q [M, H, 128] (fp8) or [M, H, 64]
+    (MXFP4) uint8, q_scale [M, H] int32 or None, w [M, H] f32, row_end [M] int32,
+    block_table_row [max_blocks] int32 -> logits [M, width] f32."""
+    cache = _paged_inputs(pool, fmt, page_size, q, q_scale, w, row_end, block_table_row.reshape(1, -1))
+    M, H = q.shape[:2]
+    if logits is None:
+        logits = torch.empty((M, (width + 3) // 4 * 4), dtype=torch.float32, device=q.device)[:, :width]
+    _abi.check(_abi.lib().idx_paged_prefill_logits(
+        ctypes.byref(cache), _ptr(q), _ptr(q_scale), _ptr(w), _ptr(row_end), _ptr(block_table_row),
+        block_table_row.numel(), M, H, _ptr(logits), logits.stride(0), width, _stream()))
+    return logits
+
+
 def _cand_rows(cand: torch.Tensor) -> None:
     _need(cand, torch.int32, "cand")
     if cand.dim() != 2 or cand.stride(1) != 1:

@@ -224,6 +224,45 @@ def paged(
     )
 
 
+@dataclass
+class PagedPrefillWorkload(PagedWorkload):
+    """A prefill chunk of one sequence over a paged K cache: ``q`` is [M, H, D], ``w``
+    [M, H], and row t scores keys [0, row_end[t]) of the sequence (B = 1)."""
+
+    row_end: np.ndarray = field(default=None)  # [M] int32
+
+    @property
+    def rows(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def M(self) -> int:
+        return self.q.shape[0]
+
+
+def paged_prefill(seed: int, M: int, N: int, H: int, width: int, topk: int, fmt: str = MXFP4, D: int = 128,
+                  page_size: int = 64, name: str = "paged prefill") -> PagedPrefillWorkload:
+    """One sequence of N cached keys in pages (random physical order) and M query rows
+    at its end: row t ends at N - M + t + 1 (causal)."""
+    base = paged(seed=seed, B=1, next_n=1, H=H, ctx_lo=0, ctx_hi=0, width=width, topk=topk, fmt=fmt, D=D,
+                 page_size=page_size, context_lens=np.array([N]), name=name)
+    rng = np.random.default_rng(seed + 1000)
+    q = rng.standard_normal((M, H, D), dtype=np.float32)
+    w = (rng.standard_normal((M, H), dtype=np.float32) / np.float32(np.sqrt(H))).astype(np.float32)
+    row_end = (N - M + 1 + np.arange(M)).astype(np.int32)
+    fields = {f: getattr(base, f) for f in base.__dataclass_fields__}
+    fields.update(q=q, w=w)
+    return PagedPrefillWorkload(**fields, row_end=row_end)
+
+
+def config6() -> PagedPrefillWorkload:
+    """Paged MXFP4 prefill chunk: one sequence, 8192 rows x 8192 keys in pages of 64,
+    causal, H = 64, top-2048 (the prefill chunk of the contiguous workload, read off
+    the paged MXFP4 cache)."""
+    return paged_prefill(seed=5, M=8192, N=8192, H=64, width=8192, topk=2048, fmt=MXFP4,
+                         name="paged mxfp4 prefill causal M=N=8192 H=64")
+
+
 # The five workloads the indexer is measured on.
 def config1() -> ContiguousWorkload:
     """Contiguous fp8, one sequence: T = 4 rows, S = 256 keys, H = 4; row t ends at S - T + t + 1; top-16."""
@@ -255,3 +294,5 @@ def config5() -> PagedWorkload:
 
 
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+# further workloads measured the same way (a second workload on the same kernels)
+EXTRA = {6: config6}

@@ -263,6 +263,29 @@ def test_two_level_checks(lib):
     assert r(P, 16, 0, 16, P, 8, 8, 16, 1, None) == OK
 
 
+def test_paged_prefill_checks(lib):
+    f = lib.idx_paged_prefill_logits
+
+    def _pf(cache=None, **kw):
+        a = dict(q=P, qsc=None, w=P, ends=P, bt=P, mb=8, M=64, H=64, out=P, os=512, width=512)
+        a.update(kw)
+        c = _cache() if cache is None else cache
+        return f(ctypes.byref(c), a["q"], a["qsc"], a["w"], a["ends"], a["bt"], a["mb"], a["M"], a["H"], a["out"],
+                 a["os"], a["width"], None)
+    assert _pf(M=-1) == SHAPE
+    assert _pf(M=0, q=None) == OK
+    assert _pf(q=None) == NULL
+    assert _pf(ends=None) == NULL
+    assert _pf(bt=None) == NULL
+    assert _pf(out=None) == NULL
+    assert _pf(cache=_cache(fmt=1)) == NULL  # MXFP4 needs query scales
+    assert _pf(qsc=P) == FORMAT
+    assert _pf(os=510) == STRIDE
+    assert _pf(q=P + 4) == STRIDE
+    assert _pf(H=0) == SHAPE
+    assert _pf(M=2 ** 20, width=2 ** 20) == SHAPE  # more walks than the prefix sums hold
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path; a GPU is visible")
 def test_valid_call_without_device_reports_device_error(lib):
     # arguments pass every host check, so the call reaches the device query, which

@@ -1,0 +1,103 @@
+"""GPU parity of the prefill chunk read straight off the paged cache
+(idx_paged_prefill_logits) against the oracle's paged logits with per-row ends: small
+cases with ragged row ends, odd row counts (a row past the two-row walks),
+both formats and several page sizes; the full 8192 x 8192 MXFP4 chunk on sampled rows;
+and the rows of the walks bit for bit against the decode entry point fed the same
+rows as two-row sequences."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import indexer
+from sparse_attention_indexer_mxfp4_amd import ops, workloads
+from tests import _inputs, _parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def _run(pi, row_end=None, width=None):
+    wl = pi.wl
+    fmt = ops.FP8 if wl.fmt == "fp8" else ops.MXFP4
+    re = wl.row_end if row_end is None else row_end
+    out = ops.idx_paged_prefill_logits(_dev(pi.pool), fmt, wl.page_size, _dev(pi.q),
+                                       None if pi.q_scale is None else _dev(pi.q_scale), _dev(wl.w),
+                                       _dev(re.astype(np.int32)), _dev(wl.block_table[0]),
+                                       wl.width if width is None else width)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle(pi, rows, row_end=None, width=None, magnitude=False):
+    wl = pi.wl
+    re = (wl.row_end if row_end is None else row_end)[rows]
+    qs = None if pi.q_scale is None else pi.q_scale[rows][None]
+    return indexer.paged_logits(pi.pool, wl.fmt, wl.page_size, wl.block_table, re, pi.q[rows][None], wl.w[rows], 1,
+                                len(rows), wl.width if width is None else width, q_scale=qs, per_row=True,
+                                magnitude=magnitude)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("M,N,H,P", [(37, 300, 64, 64), (64, 1000, 16, 16), (130, 777, 32, 128), (3, 200, 64, 64)])
+def test_paged_prefill_small(fmt, M, N, H, P):
+    width = -(-N // 64) * 64 + 32
+    wl = workloads.paged_prefill(seed=M + N + P, M=M, N=N, H=H, width=width, topk=16, fmt=fmt, page_size=P)
+    pi = _inputs.paged_inputs(wl, stride_pad=16)
+    got = _run(pi).cpu().numpy()
+    rows = np.arange(M)
+    _parity.check_logits(got, _oracle(pi, rows), _oracle(pi, rows, magnitude=True), what=f"paged prefill {fmt}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_paged_prefill_ragged_ends(fmt):
+    # row ends in any order, empty rows, ends past the sequence and past the width
+    rng = np.random.default_rng(7)
+    wl = workloads.paged_prefill(seed=8, M=45, N=900, H=64, width=1024, topk=16, fmt=fmt)
+    pi = _inputs.paged_inputs(wl)
+    re = rng.integers(0, 1200, wl.M).astype(np.int32)
+    re[:4] = [0, 1, 900, 5000]
+    got = _run(pi, row_end=re).cpu().numpy()
+    rows = np.arange(wl.M)
+    want = _oracle(pi, rows, row_end=re)
+    # ends past the sequence's 900 keys reach the rest of its last page and the
+    # block-table tail (zero bytes, as the pool was built); both sides read the same
+    # bytes, clipped to the table and the width
+    _parity.check_logits(got, want, _oracle(pi, rows, row_end=re, magnitude=True), what=f"ragged {fmt}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_paged_prefill_is_the_decode_walk(fmt):
+    # rows 2g, 2g+1 are one walk of the decode kernel over the same pages: the same
+    # bits as idx_paged_mqa_logits with those rows as a two-row (MTP) sequence
+    wl = workloads.paged_prefill(seed=9, M=48, N=700, H=64, width=768, topk=16, fmt=fmt)
+    pi = _inputs.paged_inputs(wl)
+    got = _run(pi).cpu().numpy()
+    G = wl.M // 2
+    qs = None if pi.q_scale is None else _dev(pi.q_scale.reshape(G, 2, wl.H))
+    dec, _ = ops.idx_paged_mqa_logits(_dev(pi.pool), ops.FP8 if fmt == "fp8" else ops.MXFP4, wl.page_size,
+                                      _dev(pi.q.reshape((G, 2) + pi.q.shape[1:])), qs, _dev(wl.w),
+                                      _dev(wl.row_end), _dev(np.repeat(wl.block_table, G, axis=0)), wl.width,
+                                      ctx_per_row=True)
+    np.testing.assert_array_equal(got, dec.cpu().numpy())
+
+
+def test_paged_prefill_full_chunk():
+    # the 8192 x 8192 MXFP4 chunk at full size, in the launch the benchmark times:
+    # sampled rows against the oracle, and their top-k bit for bit against the
+    # oracle's top-k on the GPU's logits
+    wl = workloads.config6()
+    pi = _inputs.paged_inputs(wl)
+    got = _run(pi)
+    k = wl.topk
+    tk = ops.idx_topk(got, None, _dev(wl.row_end), k).cpu().numpy()
+    L = got.cpu().numpy()
+    rows = np.array([0, 1, 2, 3, 63, 64, 2047, 2048, 4095, 5000, 8188, 8189, 8190, 8191])
+    want = _oracle(pi, rows)
+    _parity.check_logits(L[rows], want, _oracle(pi, rows, magnitude=True), what="config 6 sampled rows",
+                         allow_floor=False)
+    np.testing.assert_array_equal(tk[rows], indexer.topk(L[rows], None, wl.row_end[rows], k))
