@@ -9,7 +9,8 @@
 //   1. one read of the row from global memory: keys into LDS (rows up to kMaxCache)
 //      and a histogram of the top 11 bits;
 //   2. wave 0 alone finds the bin of the k-th key (lane sums of 32 bins, a DPP lane
-//      scan, one lane walks its bins in registers), then one barrier;
+//      scan and a ballot name a lane; its 32 bins, one per lane, a second scan and
+//      ballot name the bin), then one barrier;
 //   3. each wave walks its own contiguous segment of the row: it counts the keys in
 //      higher bins, compacts the keys of the selected bin into a candidate list (one
 //      LDS atomic per wave and step) tagged with the wave's number, and histograms
@@ -76,8 +77,10 @@ struct __attribute__((aligned(16))) Smem {
 
 // Wave 0 finds the digit d with (# keys above d) < kr <= (# at or above d) in
 // hist[0..NBINS) (larger digit = larger key) and publishes d and the count above
-// it; the barrier makes them visible to the workgroup. Each lane loads its NBINS/64
-// bins once and walks them in registers.
+// it; the barrier makes them visible to the workgroup. Two parallel steps, no serial
+// walk: each lane sums its NBINS/64 bins and a lane scan with a ballot names the lane
+// whose bins hold the kr-th key; then NBINS/64 lanes take one of that lane's bins
+// each (highest first), and a second scan and ballot name the bin.
 template <int NT, int NBINS>
 __device__ void select_digit(Smem<NT> &sm, const uint32_t *hist, int kr) {
   static_assert(NBINS % 256 == 0, "whole 16-byte loads per lane");
@@ -85,34 +88,25 @@ __device__ void select_digit(Smem<NT> &sm, const uint32_t *hist, int kr) {
   if ((threadIdx.x >> 6) == 0) {
     const int lane = threadIdx.x & 63;
     const int first = NBINS - (lane + 1) * kPer;  // this lane: bins [first, first + kPer), lane 0 highest
-    int c[kPer];
+    int local = 0;
 #pragma unroll
     for (int q = 0; q < kPer / 4; ++q) {
       const v4i x = *reinterpret_cast<const v4i *>(hist + first + 4 * q);
-      c[4 * q] = x[0];
-      c[4 * q + 1] = x[1];
-      c[4 * q + 2] = x[2];
-      c[4 * q + 3] = x[3];
+      local += (x[0] + x[1]) + (x[2] + x[3]);
     }
-    int local = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) local += c[j];
     const int incl = wave_incl_scan(local);
-    int run = incl - local;
-    if (run < kr && incl >= kr) {
-      int d = first, above = run;
-      bool found = false;
-#pragma unroll
-      for (int j = kPer - 1; j >= 0; --j) {
-        if (!found && run + c[j] >= kr) {
-          found = true;
-          d = first + j;
-          above = run;
-        }
-        run += c[j];
-      }
-      sm.sel_digit = d;
-      sm.sel_above = above;
+    const int run = incl - local;
+    const uint64_t hit = __ballot(run < kr && incl >= kr);
+    const int t = hit ? __builtin_ctzll(hit) : 0;  // one lane when 1 <= kr <= total
+    const int run_t = __builtin_amdgcn_readlane(run, t);
+    const int first_t = NBINS - (t + 1) * kPer;
+    const int v = lane < kPer ? int(hist[first_t + kPer - 1 - lane]) : 0;
+    const int iv = wave_incl_scan(v);
+    const uint64_t hit2 = __ballot(lane < kPer && run_t + iv >= kr);
+    const int j = hit2 ? __builtin_ctzll(hit2) : 0;
+    if (lane == j) {
+      sm.sel_digit = first_t + kPer - 1 - j;
+      sm.sel_above = run_t + iv - v;
     }
   }
   __syncthreads();
@@ -347,7 +341,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
   select_digit<NT, kBins>(sm, sm.hist, k);
 
   if (cached)
-    finish_row<NT, 4>(sm, [&](int i) { return s_keys[i]; }, n, k, out, sm.cand, Cfg<NT>::kCand);
+    finish_row<NT, 8>(sm, [&](int i) { return s_keys[i]; }, n, k, out, sm.cand, Cfg<NT>::kCand);
   else
     finish_row<NT, 16>(sm, [&](int i) { return order_key(lr[i]); }, n, k, out, s_keys, cache_cap);
 }
