@@ -290,9 +290,145 @@ __device__ void finish_row(Smem<NT> &sm, KeyAt key_at, int n, int k, int32_t *ou
   }
 }
 
+// Phases 3 to 5 for a row whose keys sit in LDS, padded with zero keys up to a whole
+// step (a zero key ranks below every real one: -inf maps to bin 3). Each lane holds
+// four consecutive keys per step, read with one 16-byte load, so a step needs no
+// bounds checks; candidates and output slots come from lane scans of per-lane counts,
+// and output stays in column order (lane-major, four columns per lane). Used when
+// the selected bin is taken whole or fits the candidate list.
+template <int NT>
+__device__ void finish_cached(Smem<NT> &sm, const uint32_t *keys, int n, int k, int32_t *out) {
+  constexpr int kStep = 256;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int seg = (n + Cfg<NT>::kWaves * kStep - 1) / (Cfg<NT>::kWaves * kStep) * kStep;
+  const int lo = min(n, wave * seg), hi = min(n, lo + seg);
+
+  const uint32_t d1 = uint32_t(sm.sel_digit);
+  const uint32_t top = (d1 << 21) | 0x1FFFFFu;  // largest key of bin d1
+  int kr = k - sm.sel_above;
+  const bool whole_bin = int(sm.hist[d1]) == kr;
+  __syncthreads();  // every thread has read hist before it is cleared below
+
+  // ---- phase 3 ----------------------------------------------------------------------
+  for (int i = tid; i < kBins; i += NT) sm.hist[i] = 0u;
+  int above = 0, match = 0;
+  for (int base = lo; base < hi; base += kStep) {
+    const v4i kv = *reinterpret_cast<const v4i *>(keys + base + 4 * lane);
+    int nc = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t key = uint32_t(kv[e]);
+      above += int(key > top);
+      nc += int((key >> 21) == d1);
+    }
+    match += nc;
+    if (!whole_bin) {
+      const int incl = wave_incl_scan(nc);
+      const int tot = __builtin_amdgcn_readlane(incl, 63);
+      if (tot != 0) {
+        int slot = 0;
+        if (lane == 0) slot = atomicAdd(&sm.ncand, tot);
+        slot = __builtin_amdgcn_readfirstlane(slot) + incl - nc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = uint32_t(kv[e]);
+          if ((key >> 21) == d1) {
+            // the list holds the bin's c1 <= kCand keys; only padding could add more,
+            // and only for a row whose k-th key sorts below -inf (a NaN)
+            atomicAdd(&sm.hist2[(key >> 10) & uint32_t(kBins - 1)], 1u);
+            if (slot < Cfg<NT>::kCand) sm.cand[slot] = (uint32_t(wave) << 21) | (key & 0x1FFFFFu);
+            ++slot;
+          }
+        }
+      }
+    }
+  }
+  above = wave_sum(above);
+  match = wave_sum(match);
+  if (lane == 0) {
+    sm.wgt[wave] = whole_bin ? above + match : above;
+    sm.weq[wave] = 0;
+  }
+  __syncthreads();
+
+  // ---- phase 4 ----------------------------------------------------------------------
+  uint32_t T;
+  if (whole_bin) {
+    T = (d1 << 21) - 1u;  // d1 >= 1: a whole bottom bin would mean n == k
+    kr = 0;
+  } else {
+    select_digit<NT, kBins>(sm, sm.hist2, kr);
+    const uint32_t p2 = (d1 << 11) | uint32_t(sm.sel_digit);
+    kr -= sm.sel_above;
+    const int nc = min(sm.ncand, Cfg<NT>::kCand);
+    for (int i = tid; i < nc; i += NT) {
+      const uint32_t key = (d1 << 21) | (sm.cand[i] & 0x1FFFFFu);
+      if ((key >> 10) == p2) atomicAdd(&sm.hist[key & 1023u], 1u);
+    }
+    __syncthreads();
+    select_digit<NT, 1024>(sm, sm.hist, kr);
+    T = (p2 << 10) | uint32_t(sm.sel_digit);
+    kr -= sm.sel_above;  // ties (keys equal to T) still to take, >= 1
+    for (int i = tid; i < nc; i += NT) {
+      const uint32_t c = sm.cand[i];
+      const uint32_t key = (d1 << 21) | (c & 0x1FFFFFu);
+      if (key > T)
+        atomicAdd(&sm.wgt[c >> 21], 1);
+      else if (key == T)
+        atomicAdd(&sm.weq[c >> 21], 1);
+    }
+    __syncthreads();
+  }
+
+  // ---- phase 5 ----------------------------------------------------------------------
+  int gt_before = 0, eq_before = 0;
+  for (int w = 0; w < wave; ++w) {
+    gt_before += sm.wgt[w];
+    eq_before += sm.weq[w];
+  }
+  int pos = gt_before + min(eq_before, kr);
+  int eq_run = eq_before;
+  for (int base = lo; base < hi; base += kStep) {
+    const v4i kv = *reinterpret_cast<const v4i *>(keys + base + 4 * lane);
+    bool sel[4];
+    int neq = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sel[e] = uint32_t(kv[e]) > T;
+      neq += int(uint32_t(kv[e]) == T);
+    }
+    if (__ballot(neq != 0) != 0ull) {
+      // ties in column order: rank = ties before this step + ties in earlier lanes +
+      // ties in this lane's earlier columns; the first kr ranks are taken
+      const int incl = wave_incl_scan(neq);
+      int r = eq_run + incl - neq;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (uint32_t(kv[e]) == T) {
+          sel[e] = r < kr;
+          ++r;
+        }
+      }
+      eq_run += __builtin_amdgcn_readlane(incl, 63);
+    }
+    const int ns = int(sel[0]) + int(sel[1]) + int(sel[2]) + int(sel[3]);
+    const int incl = wave_incl_scan(ns);
+    int p = pos + incl - ns;
+    const int col = base + 4 * lane;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (sel[e]) {
+        if (p < k) out[p] = col + e;
+        ++p;
+      }
+    }
+    pos += __builtin_amdgcn_readlane(incl, 63);
+  }
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
-  extern __shared__ uint32_t s_keys[];  // cache_cap keys
+  extern __shared__ __attribute__((aligned(16))) uint32_t s_keys[];  // cache_cap keys, rounded up to 256
   __shared__ Smem<NT> sm;
 
   const int tid = threadIdx.x;
@@ -337,10 +473,16 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
       }
     }
   }
+  // zero keys past the row up to a whole step of the cached walk
+  if (cached)
+    for (int i = n + tid; i < ((n + 255) & ~255); i += NT) s_keys[i] = 0u;
   __syncthreads();
   select_digit<NT, kBins>(sm, sm.hist, k);
 
-  if (cached)
+  const int c1 = int(sm.hist[sm.sel_digit]);
+  if (cached && (c1 == k - sm.sel_above || c1 <= Cfg<NT>::kCand))
+    finish_cached<NT>(sm, s_keys, n, k, out);
+  else if (cached)
     finish_row<NT, 8>(sm, [&](int i) { return s_keys[i]; }, n, k, out, sm.cand, Cfg<NT>::kCand);
   else
     finish_row<NT, 16>(sm, [&](int i) { return order_key(lr[i]); }, n, k, out, s_keys, cache_cap);
@@ -350,7 +492,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
 
 hipError_t launch_topk(const TopkArgs &a, int, hipStream_t stream) {
   const int cap = min(a.width, kMaxCache);
-  const size_t lds = size_t(cap) * sizeof(uint32_t);
+  const size_t lds = size_t((cap + 255) & ~255) * sizeof(uint32_t);  // whole steps of the cached walk
   static bool lds_raised = false;
   if (!lds_raised) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&topk_kernel<1024>),
