@@ -22,6 +22,8 @@
 // Rows too long for the key cache use the cache's LDS as their candidate list. If the
 // selected bin holds more keys than the list (heavy ties), digit 3 and the per-wave
 // counts come from extra passes over the row instead.
+#include <cstddef>
+
 #include "device.h"
 #include "launch.h"
 
@@ -449,33 +451,83 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
 
   // ---- phases 1 and 2 -------------------------------------------------------------------
   // kUnroll independent loads per thread are issued before any of them is used, so a
-  // batch costs one memory round trip
+  // batch costs one memory round trip. A 16-byte aligned row is read four keys per
+  // lane with range-checked buffer loads (zero past the row, no branch per key) and
+  // cached with one 16-byte LDS store per four keys, zero keys filling the last step.
   for (int i = tid; i < kBins; i += NT) {
     sm.hist[i] = 0u;
     sm.hist2[i] = 0u;
   }
   if (tid == 0) sm.ncand = 0;
   __syncthreads();
-  for (int base = 0; base < n; base += kUnroll * NT) {
-    float x[kUnroll];
+  const int n_pad = (n + 255) & ~255;
+  // two counters per bin, side by side in hist | hist2 (different LDS banks), picked by
+  // lane parity: lanes of one instruction that share a bin (logits crowd into few
+  // bins) collide half as often; summed into hist below
+  static_assert(offsetof(Smem<NT>, hist2) == offsetof(Smem<NT>, hist) + kBins * sizeof(uint32_t),
+                "hist2 follows hist");
+  uint32_t *pairs = sm.hist;
+  const int lane = tid & 63;
+  if ((reinterpret_cast<uintptr_t>(lr) & 15) == 0) {
+    const buffer_rsrc rs = make_rsrc(lr, uint32_t(n) * 4u);
+    constexpr int kGroups = kUnroll / 4;
+    for (int base = 0; base < n; base += kUnroll * NT) {
+      v4i x[kGroups];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int i = base + u * NT + tid;
-      x[u] = i < n ? lr[i] : 0.f;
-    }
+      for (int u = 0; u < kGroups; ++u) x[u] = buffer_load16(rs, uint32_t(base + (u * NT + tid) * 4) * 4u);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int i = base + u * NT + tid;
-      if (i < n) {
-        const uint32_t key = order_key(x[u]);
-        if (cached) s_keys[i] = key;
-        atomicAdd(&sm.hist[key >> 21], 1u);
+      for (int u = 0; u < kGroups; ++u) {
+        const int i = base + (u * NT + tid) * 4;
+        if (i < n_pad) {
+          uint32_t kk[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kk[e] = i + e < n ? order_key(__int_as_float(x[u][e])) : 0u;
+          if (cached) *reinterpret_cast<v4i *>(s_keys + i) = v4i{int(kk[0]), int(kk[1]), int(kk[2]), int(kk[3])};
+          if (i < n) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) atomicAdd(&pairs[2 * (kk[e] >> 21) + (lane & 1)], i + e < n ? 1u : 0u);
+          }
+        }
       }
     }
+  } else {
+    for (int base = 0; base < n; base += kUnroll * NT) {
+      float x[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int i = base + u * NT + tid;
+        x[u] = i < n ? lr[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int i = base + u * NT + tid;
+        if (i < n) {
+          const uint32_t key = order_key(x[u]);
+          if (cached) s_keys[i] = key;
+          atomicAdd(&pairs[2 * (key >> 21) + (lane & 1)], 1u);
+        }
+      }
+    }
+    // zero keys past the row up to a whole step of the cached walk
+    if (cached)
+      for (int i = n + tid; i < n_pad; i += NT) s_keys[i] = 0u;
   }
-  // zero keys past the row up to a whole step of the cached walk
-  if (cached)
-    for (int i = n + tid; i < ((n + 255) & ~255); i += NT) s_keys[i] = 0u;
+  __syncthreads();
+  {
+    constexpr int kPerT = kBins / NT;  // bins summed by each thread
+    uint32_t sum[kPerT];
+#pragma unroll
+    for (int j = 0; j < kPerT; ++j) {
+      const int b = tid * kPerT + j;
+      sum[j] = pairs[2 * b] + pairs[2 * b + 1];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPerT; ++j) {
+      sm.hist[tid * kPerT + j] = sum[j];
+      sm.hist2[tid * kPerT + j] = 0u;
+    }
+  }
   __syncthreads();
   select_digit<NT, kBins>(sm, sm.hist, k);
 
