@@ -123,6 +123,16 @@ __device__ __forceinline__ void segment(int n, int wave, int &lo, int &hi) {
   hi = min(n, lo + seg);
 }
 
+// Selected keys (above T) and ties counted in the segments of waves before `wave`:
+// lane w reads wave w's counts, and a lane scan sums them.
+template <int NT>
+__device__ __forceinline__ void before_wave(const Smem<NT> &sm, int wave, int lane, int &gt, int &eq) {
+  const int g = wave_incl_scan(lane < Cfg<NT>::kWaves ? sm.wgt[lane] : 0);
+  const int e = wave_incl_scan(lane < Cfg<NT>::kWaves ? sm.weq[lane] : 0);
+  gt = wave > 0 ? __builtin_amdgcn_readlane(g, wave - 1) : 0;
+  eq = wave > 0 ? __builtin_amdgcn_readlane(e, wave - 1) : 0;
+}
+
 // Phases 3 to 5 for one row, with the keys read through key_at (LDS or global) and
 // KPL keys per lane in flight per step. The candidate list `cand` holds up to
 // cand_cap entries: the small list in Smem for rows whose keys sit in LDS, the unused
@@ -256,11 +266,8 @@ __device__ void finish_row(Smem<NT> &sm, KeyAt key_at, int n, int k, int32_t *ou
   }
 
   // ---- phase 5: ordered emission ------------------------------------------------------
-  int gt_before = 0, eq_before = 0;
-  for (int w = 0; w < wave; ++w) {
-    gt_before += sm.wgt[w];
-    eq_before += sm.weq[w];
-  }
+  int gt_before, eq_before;
+  before_wave(sm, wave, lane, gt_before, eq_before);
   int pos = gt_before + min(eq_before, kr);  // output slots taken by earlier segments
   int eq_run = eq_before;                    // ties met before this point
   for (int base = lo; base < hi; base += kStep) {
@@ -383,11 +390,8 @@ __device__ void finish_cached(Smem<NT> &sm, const uint32_t *keys, int n, int k, 
   }
 
   // ---- phase 5 ----------------------------------------------------------------------
-  int gt_before = 0, eq_before = 0;
-  for (int w = 0; w < wave; ++w) {
-    gt_before += sm.wgt[w];
-    eq_before += sm.weq[w];
-  }
+  int gt_before, eq_before;
+  before_wave(sm, wave, lane, gt_before, eq_before);
   int pos = gt_before + min(eq_before, kr);
   int eq_run = eq_before;
   for (int base = lo; base < hi; base += kStep) {
