@@ -97,3 +97,25 @@ def test_topk_to_slots_after_topk_and_empty():
     np.testing.assert_array_equal(slots.cpu().numpy()[: want_p[-1]], want_s)
     e_slots, e_indptr, e_lens = ops.idx_topk_to_slots(torch.zeros((0, k), dtype=torch.int32, device=DEV), bt, P)
     assert e_indptr.cpu().tolist() == [0] and e_lens.numel() == 0
+
+
+@pytest.mark.parametrize("rows,width,k", [(1100, 4100, 300), (20, 40000, 2048)])
+def test_topk_aligned_rows(rows, width, k):
+    # rows starting on 16-byte boundaries take the vector first pass: lengths that are
+    # not multiples of 4 or of a 256-key step, the 256-thread variant (>= 1024 rows),
+    # rows whose selected bin is too large for the candidate list (all equal, or few
+    # distinct values), and rows longer than the key cache
+    rng = np.random.default_rng(rows + width)
+    L = rng.standard_normal((rows, width)).astype(np.float32)
+    L[0] = 2.5
+    L[1] = np.round(L[1])
+    L[2, ::2] = -np.inf
+    L[3] = np.float32(1e-3) * rng.integers(0, 3, width)
+    starts = 4 * rng.integers(0, width // 16, rows)
+    ends = np.minimum(starts + rng.integers(1, width, rows), width)
+    starts[:6], ends[:6] = 0, width
+    ends[6] = starts[6] + k + 1
+    ends[7] = starts[7] + 3
+    ends[8] = starts[8] + 257
+    got = _run(L, starts, ends, k)
+    np.testing.assert_array_equal(got, indexer.topk(L.astype(np.float64), starts, ends, k))
