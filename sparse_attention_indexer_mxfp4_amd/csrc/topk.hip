@@ -60,10 +60,11 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 
 __device__ __forceinline__ int wave_sum(int x) { return __builtin_amdgcn_readlane(wave_incl_scan(x), 63); }
 
-// Candidate list size: long rows (few rows, 1024 threads) get more room.
+// Candidate list size: long rows (few rows, 1024 threads) get more room, up to what
+// LDS holds beside a full key cache (160 KiB per workgroup).
 template <int NT>
 struct Cfg {
-  static constexpr int kCand = NT >= 1024 ? 2048 : 1024;
+  static constexpr int kCand = NT >= 1024 ? 3840 : 1024;
   static constexpr int kWaves = NT / 64;
 };
 
@@ -432,6 +433,153 @@ __device__ void finish_cached(Smem<NT> &sm, const uint32_t *keys, int n, int k, 
   }
 }
 
+// Phases 3 to 5 for a row of more keys than the key cache holds but at most twice as
+// many (up to 65536): LDS holds the top 16 bits of every key (zero-padded to whole
+// 512-key steps), which settle every key outside bin d1. The walk over them counts
+// the keys above the bin and lists the columns of the bin's keys; one gather from
+// global memory then fetches those keys' low 16 bits, kept beside their columns, which
+// is all digits 2 and 3 need. Once T is known, the candidates sharing T's top 16 bits
+// are re-labelled in LDS (one above T's prefix if above T, one below if below), so the
+// emission walk decides every key from its 16 bits: above T's prefix, or equal (a tie).
+template <int NT>
+__device__ void finish_half(Smem<NT> &sm, uint16_t *top16, const float *lr, int n, int k, int32_t *out) {
+  constexpr int kStep = 512;  // eight keys per lane per 16-byte read
+  constexpr int kCand = Cfg<NT>::kCand;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int seg = (n + Cfg<NT>::kWaves * kStep - 1) / (Cfg<NT>::kWaves * kStep) * kStep;
+  const int lo = min(n, wave * seg), hi = min(n, lo + seg);
+
+  const uint32_t d1 = uint32_t(sm.sel_digit);
+  int kr = k - sm.sel_above;
+  const bool whole_bin = int(sm.hist[d1]) == kr;
+  __syncthreads();  // every thread has read hist before it is cleared below
+
+  // ---- phase 3: counts above the bin, columns of the bin's keys ----------------------
+  for (int i = tid; i < kBins; i += NT) sm.hist[i] = 0u;
+  int above = 0, match = 0;
+  for (int base = lo; base < hi; base += kStep) {
+    const v4i raw = *reinterpret_cast<const v4i *>(top16 + base + 8 * lane);
+    uint32_t inbin = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t t = (uint32_t(raw[e >> 1]) >> (16 * (e & 1))) & 0xFFFFu;
+      above += int((t >> 5) > d1);
+      inbin |= uint32_t((t >> 5) == d1) << e;
+    }
+    const int nc = __builtin_popcount(inbin);
+    match += nc;
+    if (!whole_bin) {
+      const int incl = wave_incl_scan(nc);
+      const int tot = __builtin_amdgcn_readlane(incl, 63);
+      if (tot != 0) {
+        int slot = 0;
+        if (lane == 0) slot = atomicAdd(&sm.ncand, tot);
+        slot = __builtin_amdgcn_readfirstlane(slot) + incl - nc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if ((inbin >> e) & 1u) {
+            if (slot < kCand) sm.cand[slot] = uint32_t(base + 8 * lane + e);
+            ++slot;
+          }
+        }
+      }
+    }
+  }
+  above = wave_sum(above);
+  match = wave_sum(match);
+  if (lane == 0) {
+    sm.wgt[wave] = whole_bin ? above + match : above;
+    sm.weq[wave] = 0;
+  }
+  __syncthreads();
+
+  // ---- phase 4: T; per-wave counts; ambiguous candidates re-labelled ------------------
+  uint32_t T;
+  if (whole_bin) {
+    T = (d1 << 21) - 1u;  // d1 >= 1: a whole bottom bin would mean n == k
+    kr = 0;
+  } else {
+    const int nc = min(sm.ncand, kCand);
+    for (int i = tid; i < nc; i += NT) {
+      const uint32_t col = sm.cand[i];
+      const uint32_t key = order_key(lr[col]);
+      atomicAdd(&sm.hist2[(key >> 10) & uint32_t(kBins - 1)], 1u);
+      sm.cand[i] = (col << 16) | (key & 0xFFFFu);
+    }
+    __syncthreads();
+    select_digit<NT, kBins>(sm, sm.hist2, kr);
+    const uint32_t p2 = (d1 << 11) | uint32_t(sm.sel_digit);
+    kr -= sm.sel_above;
+    for (int i = tid; i < nc; i += NT) {
+      const uint32_t c = sm.cand[i];
+      const uint32_t key = (uint32_t(top16[c >> 16]) << 16) | (c & 0xFFFFu);
+      if ((key >> 10) == p2) atomicAdd(&sm.hist[key & 1023u], 1u);
+    }
+    __syncthreads();
+    select_digit<NT, 1024>(sm, sm.hist, kr);
+    T = (p2 << 10) | uint32_t(sm.sel_digit);
+    kr -= sm.sel_above;  // ties (keys equal to T) still to take, >= 1
+    const uint32_t tp = T >> 16;
+    for (int i = tid; i < nc; i += NT) {
+      const uint32_t c = sm.cand[i];
+      const uint32_t col = c >> 16;
+      const uint32_t t = top16[col];
+      const uint32_t key = (t << 16) | (c & 0xFFFFu);
+      const int w = int(col) / seg;
+      if (key > T)
+        atomicAdd(&sm.wgt[w], 1);
+      else if (key == T)
+        atomicAdd(&sm.weq[w], 1);
+      if (t == tp) top16[col] = uint16_t(key > T ? min(tp + 1u, 0xFFFFu) : key < T ? max(tp, 1u) - 1u : tp);
+    }
+    __syncthreads();
+  }
+
+  // ---- phase 5: emission from the 16-bit keys --------------------------------------
+  const uint32_t tp = T >> 16;
+  int gt_before, eq_before;
+  before_wave(sm, wave, lane, gt_before, eq_before);
+  int pos = gt_before + min(eq_before, kr);
+  int eq_run = eq_before;
+  for (int base = lo; base < hi; base += kStep) {
+    const v4i raw = *reinterpret_cast<const v4i *>(top16 + base + 8 * lane);
+    uint32_t sel = 0, eq = 0;  // bit e: column base + 8 lane + e
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t t = (uint32_t(raw[e >> 1]) >> (16 * (e & 1))) & 0xFFFFu;
+      sel |= uint32_t(t > tp) << e;
+      eq |= uint32_t(t == tp) << e;
+    }
+    if (__ballot(eq != 0u) != 0ull) {
+      const int neq = __builtin_popcount(eq);
+      const int incl = wave_incl_scan(neq);
+      int r = eq_run + incl - neq;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if ((eq >> e) & 1u) {
+          sel |= uint32_t(r < kr) << e;
+          ++r;
+        }
+      }
+      eq_run += __builtin_amdgcn_readlane(incl, 63);
+    }
+    const int ns = __builtin_popcount(sel);
+    const int incl = wave_incl_scan(ns);
+    int p = pos + incl - ns;
+    const int col = base + 8 * lane;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if ((sel >> e) & 1u) {
+        if (p < k) out[p] = col + e;
+        ++p;
+      }
+    }
+    pos += __builtin_amdgcn_readlane(incl, 63);
+  }
+}
+
+static_assert(sizeof(Smem<1024>) + kMaxCache * sizeof(uint32_t) <= 160 * 1024, "LDS of a workgroup");
+
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
   extern __shared__ __attribute__((aligned(16))) uint32_t s_keys[];  // cache_cap keys, rounded up to 256
@@ -452,6 +600,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
   }
   const float *lr = a.logits + int64_t(row) * a.logits_row_stride + start;
   const bool cached = n <= cache_cap;
+  const bool half = !cached && n <= 2 * cache_cap;  // top 16 bits of every key fit the cache
+  uint16_t *s_top16 = reinterpret_cast<uint16_t *>(s_keys);
 
   // ---- phases 1 and 2 -------------------------------------------------------------------
   // kUnroll independent loads per thread are issued before any of them is used, so a
@@ -464,7 +614,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
   }
   if (tid == 0) sm.ncand = 0;
   __syncthreads();
-  const int n_pad = (n + 255) & ~255;
+  const int n_pad = half ? (n + 511) & ~511 : (n + 255) & ~255;  // whole steps of the cached walks
   // two counters per bin, side by side in hist | hist2 (different LDS banks), picked by
   // lane parity: lanes of one instruction that share a bin (logits crowd into few
   // bins) collide half as often; summed into hist below
@@ -487,6 +637,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) kk[e] = i + e < n ? order_key(__int_as_float(x[u][e])) : 0u;
           if (cached) *reinterpret_cast<v4i *>(s_keys + i) = v4i{int(kk[0]), int(kk[1]), int(kk[2]), int(kk[3])};
+          if (half)
+            *reinterpret_cast<uint2 *>(s_top16 + i) = make_uint2((kk[0] >> 16) | (kk[1] & 0xFFFF0000u),
+                                                                 (kk[2] >> 16) | (kk[3] & 0xFFFF0000u));
           if (i < n) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) atomicAdd(&pairs[2 * (kk[e] >> 21) + (lane & 1)], i + e < n ? 1u : 0u);
@@ -508,13 +661,16 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
         if (i < n) {
           const uint32_t key = order_key(x[u]);
           if (cached) s_keys[i] = key;
+          if (half) s_top16[i] = uint16_t(key >> 16);
           atomicAdd(&pairs[2 * (key >> 21) + (lane & 1)], 1u);
         }
       }
     }
-    // zero keys past the row up to a whole step of the cached walk
+    // zero keys past the row up to a whole step of the cached walks
     if (cached)
       for (int i = n + tid; i < n_pad; i += NT) s_keys[i] = 0u;
+    if (half)
+      for (int i = n + tid; i < n_pad; i += NT) s_top16[i] = 0u;
   }
   __syncthreads();
   {
@@ -540,6 +696,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
     finish_cached<NT>(sm, s_keys, n, k, out);
   else if (cached)
     finish_row<NT, 8>(sm, [&](int i) { return s_keys[i]; }, n, k, out, sm.cand, Cfg<NT>::kCand);
+  else if (half && (c1 == k - sm.sel_above || c1 <= Cfg<NT>::kCand))
+    finish_half<NT>(sm, s_top16, lr, n, k, out);
   else
     finish_row<NT, 16>(sm, [&](int i) { return order_key(lr[i]); }, n, k, out, s_keys, cache_cap);
 }
