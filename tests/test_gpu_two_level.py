@@ -180,3 +180,37 @@ def test_two_level_step(fmt):
     ow = candidates.remap_compact_topk(indexer.topk(candidates.gather_logits(want, e, c, block), None, pe, k), c, block)
     _parity.check_topk(got, ow, candidates.candidate_mask(want, e, c, block), np.zeros(wl.rows, np.int64),
                        what=f"two-level {fmt}")
+
+
+@pytest.mark.parametrize("cfg", [5, 3])
+def test_two_level_full_size(cfg):
+    # the two-level step of the benchmark (pool of 64 blocks of 64 keys) on the full
+    # MXFP4 decode and fp8 MTP workloads: every step bit for bit against the oracle
+    # applied to the GPU's own inputs of that step, and the source logits against the
+    # oracle's exact ones on sampled whole sequences
+    wl = workloads.CONFIGS[cfg]()
+    pi = _inputs.paged_inputs(wl)
+    block, n, k = 64, 64, wl.topk
+    dense, ends, bm = _source(pi, block)
+    cand = ops.idx_candidate_blocks(bm, ends, block, n)
+    pool, pool_end = ops.idx_paged_mqa_logits_gather(*_args(pi), cand, block)
+    tk = ops.idx_remap_compact_topk(ops.idx_topk(pool, None, pool_end, k), cand, block)
+    torch.cuda.synchronize()
+    D, e, B, c = dense.cpu().numpy(), ends.cpu().numpy(), bm.cpu().numpy(), cand.cpu().numpy()
+    np.testing.assert_array_equal(B, candidates.block_scores(D, e, block).astype(np.float32))
+    np.testing.assert_array_equal(c, candidates.candidate_blocks(B, e, block, n))
+    P = pool.cpu().numpy()
+    np.testing.assert_array_equal(P, candidates.gather_logits(D, e, c, block).astype(np.float32))
+    pe = candidates.gather_row_ends(c, e, block, wl.rows)
+    np.testing.assert_array_equal(pool_end.cpu().numpy(), pe)
+    rows = np.arange(0, wl.rows, max(1, wl.rows // 12))
+    got = tk.cpu().numpy()[rows]
+    want = candidates.remap_compact_topk(indexer.topk(P[rows].astype(np.float64), None, pe[rows], k), c[rows], block)
+    np.testing.assert_array_equal(got, want)
+    seqs = sorted(set(int(r) // wl.next_n for r in rows[:4]))
+    for b in seqs:
+        sub = np.arange(b * wl.next_n, (b + 1) * wl.next_n)
+        exact = indexer.paged_logits(pi.pool, wl.fmt, wl.page_size, wl.block_table[b:b + 1], wl.context_lens[b:b + 1],
+                                     pi.q[b:b + 1], wl.w[sub], 1, wl.next_n, wl.width,
+                                     q_scale=None if pi.q_scale is None else pi.q_scale[b:b + 1])
+        _parity.check_logits(D[sub], exact, what=f"config {cfg} source sequence {b}", allow_floor=False)
