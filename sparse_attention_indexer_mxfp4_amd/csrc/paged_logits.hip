@@ -456,10 +456,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
   int qb = -1;  // sequence whose queries are loaded
   auto stream = [&](const int u0, const int u1) {
     if (u0 >= u1) return;
+    int ib = find_seq(s_pref, S, u0);  // coordinates of the next chunk to issue
+    // The first sequence's queries go out right behind the block-table load and
+    // ahead of the K loads: the table's wait does not cover them (a burst of query
+    // loads issued first held the table back by over a microsecond), and scoring the
+    // first chunk waits on its K loads only (a query load issued behind the K loads
+    // would hold that wait until every chunk in flight and the tail stores issued
+    // before it had landed).
     int pg_base = u0;
     int pp = -1;
     int pg = load_pages(pg_base, pp);
-    int ib = find_seq(s_pref, S, u0);  // coordinates of the next chunk to issue
+    load_queries(ib);
+    qb = ib;
     int ic = u0 - s_pref[ib];
     int iu = u0;
     constexpr int kRing = ring_depth<FMT, NR>();
