@@ -5,10 +5,10 @@
 // fp8_mqa_logits_torch. k_scale > 0, so it is applied once per (t, s) after the head
 // sum instead of once per head.
 //
-// The contraction runs on the fp8 matrix cores; what limits it on gfx950 is the
-// per-element epilogue, because the VALU and the matrix core overlap only partly (an
-// MFMA holds off vector issue for most of its cycles): a ReLU plus a multiply-add per
-// (t, h, s) costs as much time as the MFMA that produced it.
+// The contraction runs on the fp8 matrix cores; the per-element epilogue competes
+// with them for instruction issue: about four vector multiply-adds fit beside each
+// 16x16x128 MFMA (which occupies the issue port for roughly half of its 32 cycles),
+// while a ReLU plus a multiply-add per (t, h, s) would need eight.
 // The kernel therefore uses max(x, 0) = (x + |x|) / 2:
 //
 //   sum_h w_h max(S_h, 0) = 1/2 * ( sum_h w_h |S_h|  +  sum_h w_h S_h ).

@@ -52,6 +52,21 @@ def test_mqa_logits_causal_tiles():
     _parity.check_logits(got, want, what="causal 300", allow_floor=False)
 
 
+def test_mqa_logits_many_tiles():
+    # more row tiles than three rounds of resident workgroups: each workgroup scores
+    # several tiles in snake order; every row is compared
+    M, N = 12300, 200
+    rng = np.random.default_rng(77)
+    starts = rng.integers(0, 40, M)
+    ends = np.minimum(N, np.arange(M) % (N + 7))
+    wl = workloads.contiguous(seed=78, M=M, N=N, H=8, starts=starts, ends=ends)
+    ci = _inputs.contig_inputs(wl)
+    got = _run_contig(ci, wl.ks, wl.ke)
+    want = indexer.mqa_logits_fp8(ci.q, ci.k, ci.k_scale, wl.w, wl.ks, wl.ke)
+    mag = indexer.mqa_logits_fp8(ci.q, ci.k, ci.k_scale, wl.w, wl.ks, wl.ke, magnitude=True)
+    _parity.check_logits(got, want, mag, what=f"mqa M={M} N={N}")
+
+
 def test_mqa_logits_config1():
     wl = workloads.config1()
     ci = _inputs.contig_inputs(wl)
