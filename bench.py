@@ -34,6 +34,7 @@ COPY_BYTES = 2**30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {  # kernel -> sources whose text the measured counters belong to
     "paged_logits_kernel": ["paged_logits.hip", "device.h"],
+    "paged_prefill_fp4_kernel": ["paged_prefill.hip", "device.h"],
     "mqa_logits_fp8_kernel": ["mqa_logits.hip", "device.h"],
 }
 
@@ -498,8 +499,8 @@ def prefill_paged_main(args, wl, ops, torch, dev):
                    "topk_ms": round(topk_ms, 4), "k_cache_copies": copies},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP4_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / FP4_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("paged_logits_kernel", wl.name),
-                     "kernel": "paged_logits_kernel (two-row walks)", "kernel_ms": round(logits_ms, 4),
+                     "traffic": measured_traffic("paged_prefill_fp4_kernel", wl.name),
+                     "kernel": "paged_prefill_fp4_kernel", "kernel_ms": round(logits_ms, 4),
                      "algorithmic_flop": flop, "algorithmic_bytes": nbytes},
     }
     if not args.no_cpu_baseline:

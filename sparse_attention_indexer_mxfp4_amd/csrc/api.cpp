@@ -172,9 +172,10 @@ idx_status idx_paged_prefill_logits(const idx_paged_cache *cache, const void *q,
                                     const float *w, const int32_t *row_end, const int32_t *block_table,
                                     int32_t max_blocks, int32_t M, int32_t H, float *logits,
                                     int64_t logits_row_stride, int32_t width, hipStream_t stream) {
-  // pairs of consecutive rows share one walk over the sequence's pages (two rows per
-  // walk keep two waves per SIMD; measured on the 8192 x 8192 MXFP4 chunk: 524 us
-  // against 650 us for one row and 783 us for four); an odd last row walks alone
+  // fp8 pages (and more than 64 heads): pairs of consecutive rows share one walk over
+  // the sequence's pages (two rows per walk keep two waves per SIMD; measured on the
+  // 8192 x 8192 MXFP4 chunk: 524 us against 650 us for one row and 783 us for four);
+  // an odd last row walks alone
   constexpr int32_t kWalkRows = 2;
   if (M < 0) return IDX_ERR_SHAPE;
   const int32_t groups = M / kWalkRows, tail = M % kWalkRows;
@@ -186,6 +187,12 @@ idx_status idx_paged_prefill_logits(const idx_paged_cache *cache, const void *q,
   if (int64_t(M) * ((int64_t(width) + 63) / 64) > INT32_MAX) return IDX_ERR_SHAPE;
   int cus = 0;
   if ((s = current_device(&cus)) != IDX_OK) return s;
+  if (cache->fmt == IDX_KV_MXFP4_E2M1 && H <= 64) {
+    // MXFP4 pages: eight rows per workgroup share each key chunk through LDS
+    const idx::PagedArgs a = paged_args(cache, q, q_scale, w, row_end, 1, block_table, 0, max_blocks, M, 1, H,
+                                        logits, logits_row_stride, width, nullptr);
+    return launched(idx::launch_paged_prefill_fp4(a, cus, stream));
+  }
   const int64_t qrow = int64_t(H) * (cache->fmt == IDX_KV_FP8_E4M3 ? cache->head_dim : cache->head_dim / 2);
   if (groups > 0) {
     idx::PagedArgs a = paged_args(cache, q, q_scale, w, row_end, 1, block_table, 0, max_blocks, groups, kWalkRows,

@@ -148,6 +148,9 @@ struct SlotsArgs {
 
 hipError_t launch_mqa_logits(const MqaArgs &a, int num_cus, hipStream_t stream);
 hipError_t launch_paged_logits(const PagedArgs &a, int num_cus, hipStream_t stream);
+// a prefill chunk of one sequence off its MXFP4 pages: rows a.B, row ends in
+// a.context_lens, the sequence's pages in a.block_table; H <= 64
+hipError_t launch_paged_prefill_fp4(const PagedArgs &a, int num_cus, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs &a, int num_cus, hipStream_t stream);
 hipError_t launch_k_store(const KStoreArgs &a, hipStream_t stream);
 hipError_t launch_q_quant(const QQuantArgs &a, hipStream_t stream);

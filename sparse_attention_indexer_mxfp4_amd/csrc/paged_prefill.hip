@@ -1,0 +1,231 @@
+// A prefill chunk of one sequence scored straight off its MXFP4 pages: M query rows,
+// row r scoring keys [0, end_r) of the sequence through its block-table row, with no
+// gather of K (page "vllm.v1.attention.ops.rocm_paged_mxfp4_indexer", module
+// description and rocm_mxfp4_sparse_attn_indexer: prefill chunks read the paged cache
+// in place). Every logit is the one the paged decode walk computes:
+// I[r, s] = sum_h w[r, h] * max(sum_j 2^(eq - 127) 2^(ek - 127) q_hj . k_sj, 0).
+//
+// Unlike decode, many rows share each key, so the work is a dense contraction with a
+// causal mask. A workgroup owns 8 query rows (two per wave, queries and their block
+// scales held as MFMA A operands) and one key split, and streams the sequence's keys
+// through two LDS buffers in 64-key chunks shared by its four waves. A chunk is four
+// 16-key runs: wave w fetches run w of the chunk - its page from the block table
+// (one scalar load: the run lies inside one page), then the run's kilobyte (lane L's
+// 16 bytes at 16L, already in the scaled MFMA's B-operand order) and its 64 e8m0
+// bytes (lane L's own block scale) - two chunks ahead of their scoring. Scoring runs
+// the scaled fp4 MFMA (16 heads x 16 keys x 128 channels) with the MFMAs of key group
+// kg+1 interleaved with the ReLU-weighted head sums of group kg, then the transposed
+// permlane reduction that leaves key L of the chunk in lane L and one 256-byte store
+// per row. Columns of the split past the rows' longest end are filled with -inf
+// without touching K. Row tiles are launched longest-first (the causal chunk's last
+// rows see the most keys).
+#include <climits>
+
+#include "device.h"
+#include "launch.h"
+
+namespace idx {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kRowsPerWave = 2;
+constexpr int kRowsPerWG = kWaves * kRowsPerWave;
+constexpr int kChunk = 64;
+constexpr int kDepth = 2;  // chunks requested ahead of the one being scored
+
+// -inf into row[from, to); `from` is a multiple of 4 and the row is 16-byte aligned.
+__device__ void fill_ninf(float *row, int from, int to, int lane) {
+  const float ninf = neg_inf();
+  for (int c = from + 4 * lane; c < to; c += 256) {
+    if (c + 4 <= to) {
+      __builtin_nontemporal_store(v4f{ninf, ninf, ninf, ninf}, reinterpret_cast<v4f *>(row + c));
+    } else {
+      for (int i = 0; i < 4 && c + i < to; ++i) __builtin_nontemporal_store(ninf, row + c + i);
+    }
+  }
+}
+
+template <int HT>
+__global__ __launch_bounds__(256, 2) void paged_prefill_fp4_kernel(PagedArgs a, int split_keys) {
+  __shared__ __attribute__((aligned(16))) uint8_t sk[2][kChunk * 64];  // run kg at kg * 1024, lane L at 16 L
+  __shared__ uint8_t ss[2][kChunk * 4];                                // run kg's scale bytes at kg * 64 + L
+  __shared__ int s_hi;
+
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int M = a.B;
+  const int P = a.page_size;
+  const int cap = int(min(int64_t(a.width), int64_t(a.max_blocks) * P));
+  const int tile = int(gridDim.x) - 1 - int(blockIdx.x);
+  const int row0 = tile * kRowsPerWG;
+  const int s0 = int(blockIdx.y) * split_keys;
+  const int s1 = min(a.width, s0 + split_keys);
+
+  if (tid < 64) {
+    int hi = 0;
+    if (lane < kRowsPerWG && row0 + lane < M) hi = min(max(a.context_lens[row0 + lane], 0), cap);
+    for (int off = 4; off > 0; off >>= 1) hi = max(hi, __shfl_xor(hi, off));
+    if (lane == 0) s_hi = hi;
+  }
+
+  // ---- this wave's rows: queries and block scales as A operands, weights in the
+  // C-layout head order (lane (g, n) holds heads 16 ht + 4 g + j of its C rows) --------
+  const int r_base = row0 + wave * kRowsPerWave;
+  v8i qa[kRowsPerWave][HT];
+  int qs[kRowsPerWave][HT];
+  float wv[kRowsPerWave][HT][4];
+  int rend[kRowsPerWave];
+  bool active[kRowsPerWave];
+#pragma unroll
+  for (int rr = 0; rr < kRowsPerWave; ++rr) {
+    const int r = r_base + rr;
+    active[rr] = r < M;
+    rend[rr] = active[rr] ? min(max(a.context_lens[r], 0), cap) : 0;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int h = ht * 16 + n;
+      if (active[rr] && h < a.H) {
+        const v4i z = {0, 0, 0, 0};
+        qa[rr][ht] = cat(load16(a.q + (int64_t(r) * a.H + h) * 64 + g * 16), z);
+        qs[rr][ht] = (a.q_scale[int64_t(r) * a.H + h] >> (8 * g)) & 0xFF;
+      } else {
+        qa[rr][ht] = zero8();
+        qs[rr][ht] = 127;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int hh = ht * 16 + 4 * g + j;
+        wv[rr][ht][j] = (active[rr] && hh < a.H) ? a.w[int64_t(r) * a.H + hh] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // chunks [s0, c_end) of the split reach some row of the tile; the rest is -inf
+  const int hi = min(s_hi, s1);
+  const int c_end = hi > s0 ? min(((hi + kChunk - 1) / kChunk) * kChunk, s1) : s0;
+#pragma unroll
+  for (int rr = 0; rr < kRowsPerWave; ++rr)
+    if (active[rr]) fill_ninf(a.logits + int64_t(r_base + rr) * a.logits_row_stride, c_end, s1, lane);
+
+  // wave w fetches run w of a chunk: the page of keys [c + 16 w, c + 16 w + 16) (inside
+  // one page, since 16 divides the page size), then the run's values and scales; runs
+  // at or past the tile's longest end are not read (zero values, unit scales)
+  struct Fetch {
+    v4i kv;
+    int ks;
+  };
+  auto fetch = [&](Fetch &f, int c) {
+    const int pos = c + 16 * wave;
+    f.kv = v4i{0, 0, 0, 0};
+    f.ks = 127;
+    if (pos < hi) {
+      const int pi = a.page_shift >= 0 ? pos >> a.page_shift : pos / P;
+      const int e0 = a.page_shift >= 0 ? pos & (P - 1) : pos % P;
+      const int page = min(max(a.block_table[pi], 0), a.num_pages - 1);
+      const uint8_t *pb = a.base + int64_t(page) * a.page_stride;
+      const int run = e0 >> 4;
+      f.kv = load16(pb + run * 1024 + lane * 16);
+      f.ks = pb[P * 64 + run * 64 + lane];
+    }
+  };
+  auto stage = [&](const Fetch &f, int buf) {
+    *reinterpret_cast<v4i *>(&sk[buf][wave * 1024 + lane * 16]) = f.kv;
+    ss[buf][wave * 64 + lane] = uint8_t(f.ks);
+  };
+
+  // Scoring of one chunk as a fixed schedule: the MFMAs of key group kg+1 are issued
+  // one at a time, each followed by the ReLU-weighted sums of one (row, head tile) of
+  // group kg; scheduling fences keep the compiler from regrouping them.
+  auto score = [&](int c, int buf) {
+    v8i kb[4];
+    int ksb[4];
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      const v4i z = {0, 0, 0, 0};
+      kb[kg] = cat(*reinterpret_cast<const v4i *>(&sk[buf][kg * 1024 + lane * 16]), z);
+      ksb[kg] = ss[buf][kg * 64 + lane];
+    }
+    float part[kRowsPerWave][4];
+    v4f sv[2][kRowsPerWave][HT];
+#pragma unroll
+    for (int rr = 0; rr < kRowsPerWave; ++rr)
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) sv[0][rr][ht] = mfma_fp4(qa[rr][ht], kb[0], qs[rr][ht], ksb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      const int cur = kg & 1, nxt = cur ^ 1;
+      float acc[kRowsPerWave];
+#pragma unroll
+      for (int rr = 0; rr < kRowsPerWave; ++rr) acc[rr] = 0.f;
+#pragma unroll
+      for (int u = 0; u < kRowsPerWave * HT; ++u) {
+        const int rr = u % kRowsPerWave, ht = u / kRowsPerWave;
+        if (kg < 3) sv[nxt][rr][ht] = mfma_fp4(qa[rr][ht], kb[kg + 1], qs[rr][ht], ksb[kg + 1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[rr] = fmaf(wv[rr][ht][j], relu(sv[cur][rr][ht][j]), acc[rr]);
+        pin(acc[rr]);  // computed here, not sunk towards its use
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int rr = 0; rr < kRowsPerWave; ++rr) part[rr][kg] = acc[rr];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int col = c + lane;
+#pragma unroll
+    for (int rr = 0; rr < kRowsPerWave; ++rr) {
+      const float val = transpose_reduce4(part[rr]);
+      if (active[rr] && col < c_end)
+        a.logits[int64_t(r_base + rr) * a.logits_row_stride + col] = col < rend[rr] ? val : neg_inf();
+    }
+  };
+
+  Fetch f[kDepth];
+  if (s0 < c_end) {
+    fetch(f[0], s0);
+    stage(f[0], 0);
+#pragma unroll
+    for (int u = 1; u < kDepth; ++u) fetch(f[u], s0 + u * kChunk);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int c = s0; c < c_end; c += kDepth * kChunk) {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      // buffer `buf` holds chunk cc; set u is free, set (u + 1) % kDepth holds cc + 64
+      const int cc = c + u * kChunk;
+      if (cc >= c_end) break;
+      fetch(f[u], cc + kDepth * kChunk);
+      score(cc, buf);
+      stage(f[(u + 1) % kDepth], buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_paged_prefill_fp4(const PagedArgs &a, int num_cus, hipStream_t stream) {
+  const int tiles = (a.B + kRowsPerWG - 1) / kRowsPerWG;
+  const int nchunks = (a.width + kChunk - 1) / kChunk;
+  int splits = (4 * num_cus + tiles - 1) / tiles;
+  splits = max(1, min(splits, nchunks));
+  const int split_keys = ((nchunks + splits - 1) / splits) * kChunk;
+  splits = (a.width + split_keys - 1) / split_keys;
+  const dim3 grid(tiles, splits);
+  const int ht = (a.H + 15) / 16;
+  if (ht <= 1)
+    paged_prefill_fp4_kernel<1><<<grid, 256, 0, stream>>>(a, split_keys);
+  else if (ht <= 2)
+    paged_prefill_fp4_kernel<2><<<grid, 256, 0, stream>>>(a, split_keys);
+  else
+    paged_prefill_fp4_kernel<4><<<grid, 256, 0, stream>>>(a, split_keys);
+  return hipGetLastError();
+}
+
+}  // namespace idx

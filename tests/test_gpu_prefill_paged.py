@@ -1,9 +1,10 @@
 """GPU parity of the prefill chunk read straight off the paged cache
 (idx_paged_prefill_logits) against the oracle's paged logits with per-row ends: small
-cases with ragged row ends, odd row counts (a row past the two-row walks),
-both formats and several page sizes; the full 8192 x 8192 MXFP4 chunk on sampled rows;
-and the rows of the walks bit for bit against the decode entry point fed the same
-rows as two-row sequences."""
+cases with ragged row ends, odd row counts, head counts that are not a multiple of 16,
+both formats and several page sizes (one not a power of two); the full 8192 x 8192
+MXFP4 chunk on sampled rows; and every row bit for bit against the decode entry point
+fed the same rows as two-row sequences (the MXFP4 chunk kernel sums each logit in the
+decode walk's order)."""
 
 import numpy as np
 import pytest
@@ -43,7 +44,8 @@ def _oracle(pi, rows, row_end=None, width=None, magnitude=False):
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
-@pytest.mark.parametrize("M,N,H,P", [(37, 300, 64, 64), (64, 1000, 16, 16), (130, 777, 32, 128), (3, 200, 64, 64)])
+@pytest.mark.parametrize("M,N,H,P", [(37, 300, 64, 64), (64, 1000, 16, 16), (130, 777, 32, 128), (3, 200, 64, 64),
+                                     (21, 500, 24, 48)])
 def test_paged_prefill_small(fmt, M, N, H, P):
     width = -(-N // 64) * 64 + 32
     wl = workloads.paged_prefill(seed=M + N + P, M=M, N=N, H=H, width=width, topk=16, fmt=fmt, page_size=P)
