@@ -302,7 +302,11 @@ idx_status idx_topk_to_slots(const int32_t *topk, int64_t topk_row_stride, int32
  * block-table row, with no gather of K. Page "vllm.v1.attention.ops.rocm_paged_mxfp4_indexer",
  * module description (the kernel reads the paged K cache in place, prefill included)
  * and rocm_mxfp4_sparse_attn_indexer (prefill chunks walk the same cache as decode).
- * Every row's logit of key s is computed exactly as idx_paged_mqa_logits computes it.
+ * Every row's logit of key s is the one idx_paged_mqa_logits defines; up to 64 heads
+ * (MXFP4) or 128 (fp8) the rows are scored eight at a time with each key chunk shared
+ * through LDS and the ReLU split as (x + |x|) / 2, so values agree with the decode
+ * walk up to float32 rounding (bit for bit for MXFP4 with more than 64 heads, which
+ * walks rows in pairs).
  *
  *   cache         the paged K cache (fp8 or MXFP4), as idx_paged_mqa_logits.
  *   q             [M, H, D] e4m3 (fp8) or [M, H, D/2] packed e2m1 (MXFP4), 16-byte aligned.
@@ -313,7 +317,7 @@ idx_status idx_topk_to_slots(const int32_t *topk, int64_t topk_row_stride, int32
  *   block_table   [max_blocks] int32: the sequence's pages.
  *   logits        [M, width] fp32 with logits_row_stride (multiple of 4, 16-byte
  *                 aligned); -inf at and past each row's end.
- *   Limits: M >= 0; M * ceil(width / 64) < 2^31; rows are walked two at a time.
+ *   Limits: M >= 0; M * ceil(width / 64) < 2^31; 1 <= H <= 128.
  */
 idx_status idx_paged_prefill_logits(const idx_paged_cache *cache, const void *q, const int32_t *q_scale,
                                     const float *w, const int32_t *row_end, const int32_t *block_table,

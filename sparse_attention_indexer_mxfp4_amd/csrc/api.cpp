@@ -2,6 +2,7 @@
 // check, and the launch of each call's kernels on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 
@@ -172,7 +173,7 @@ idx_status idx_paged_prefill_logits(const idx_paged_cache *cache, const void *q,
                                     const float *w, const int32_t *row_end, const int32_t *block_table,
                                     int32_t max_blocks, int32_t M, int32_t H, float *logits,
                                     int64_t logits_row_stride, int32_t width, hipStream_t stream) {
-  // fp8 pages (and more than 64 heads): pairs of consecutive rows share one walk over
+  // MXFP4 pages with more than 64 heads: pairs of consecutive rows share one walk over
   // the sequence's pages (two rows per walk keep two waves per SIMD; measured on the
   // 8192 x 8192 MXFP4 chunk: 524 us against 650 us for one row and 783 us for four);
   // an odd last row walks alone
@@ -192,6 +193,31 @@ idx_status idx_paged_prefill_logits(const idx_paged_cache *cache, const void *q,
     const idx::PagedArgs a = paged_args(cache, q, q_scale, w, row_end, 1, block_table, 0, max_blocks, M, 1, H,
                                         logits, logits_row_stride, width, nullptr);
     return launched(idx::launch_paged_prefill_fp4(a, cus, stream));
+  }
+  if (cache->fmt == IDX_KV_FP8_E4M3) {
+    // fp8 pages: the contiguous prefill kernel with its keys read through the block table
+    idx::MqaArgs a{};
+    a.q = static_cast<const uint8_t *>(q);
+    a.q_row_stride = int64_t(H) * cache->head_dim;
+    a.k_row_stride = cache->head_dim;
+    a.w = w;
+    a.w_row_stride = H;
+    a.row_end = row_end;  // row_start stays NULL: every row starts at key 0
+    a.M = M;
+    a.N = width;
+    a.H = H;
+    a.logits = logits;
+    a.logits_row_stride = logits_row_stride;
+    a.kbase = static_cast<const uint8_t *>(cache->base);
+    a.page_stride = cache->page_stride_bytes;
+    a.block_table = block_table;
+    a.page_size = cache->page_size;
+    a.page_shift = -1;
+    for (int sh = 4; sh <= 10; ++sh)
+      if (cache->page_size == (1 << sh)) a.page_shift = sh;
+    a.num_pages = cache->num_pages;
+    a.key_limit = int32_t(std::min<int64_t>(width, int64_t(max_blocks) * cache->page_size));
+    return launched(idx::launch_mqa_logits(a, cus, stream));
   }
   const int64_t qrow = int64_t(H) * (cache->fmt == IDX_KV_FP8_E4M3 ? cache->head_dim : cache->head_dim / 2);
   if (groups > 0) {

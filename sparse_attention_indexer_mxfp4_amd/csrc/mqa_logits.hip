@@ -31,6 +31,10 @@
 // and one coalesced 256-byte row segment per chunk is stored. Columns of the split
 // outside the rows' key range are filled with -inf without touching K. Row tiles are
 // launched longest-first so a causal chunk's long rows do not trail the grid.
+//
+// The same kernel scores a prefill chunk straight off an fp8 paged cache (PAGED): a
+// chunk's keys are then read from the pages the sequence's block table names, with
+// the same LDS staging and epilogue.
 #include <climits>
 
 #include "device.h"
@@ -72,7 +76,7 @@ __device__ __forceinline__ void reduce_scatter_step(float (&x)[32], bool upper) 
   }
 }
 
-template <int HT>
+template <int HT, bool PAGED>
 __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int split_keys) {
   __shared__ __attribute__((aligned(16))) uint8_t sk[2][kChunk * kKeyStride];
   __shared__ float ss[2][kChunk];
@@ -88,12 +92,13 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
   const int row0 = tile * kRowsPerWG;
   const int s0 = int(blockIdx.y) * split_keys;
   const int s1 = min(a.N, s0 + split_keys);
+  const int klim = PAGED ? a.key_limit : a.N;  // keys that exist
 
   if (tid < 64) {
     int lo = INT_MAX, hi = INT_MIN;
     if (lane < kRowsPerWG && row0 + lane < a.M) {
-      const int rl = max(a.row_start[row0 + lane], 0);
-      const int rh = min(a.row_end[row0 + lane], a.N);
+      const int rl = a.row_start ? max(a.row_start[row0 + lane], 0) : 0;
+      const int rh = min(a.row_end[row0 + lane], klim);
       if (rl < rh) {
         lo = rl;
         hi = rh;
@@ -120,8 +125,8 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
   for (int rr = 0; rr < kRowsPerWave; ++rr) {
     const int r = r_base + rr;
     active[rr] = r < a.M;
-    rlo[rr] = active[rr] ? a.row_start[r] : 0;
-    rhi[rr] = active[rr] ? min(a.row_end[r], a.N) : 0;
+    rlo[rr] = active[rr] && a.row_start ? a.row_start[r] : 0;
+    rhi[rr] = active[rr] ? min(a.row_end[r], klim) : 0;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       const int h = ht * 16 + n;
@@ -224,17 +229,53 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
     v4i kv[2];
     float ks;
   };
-  auto fetch = [&](Fetch &f, int c) {
-    const int64_t left = max(int64_t(a.N) - c, int64_t(0));
-    const buffer_rsrc kr = make_rsrc(a.k + int64_t(c) * a.k_row_stride, range_bytes(left * a.k_row_stride));
-    const buffer_rsrc sr = make_rsrc(a.k_scale + c, range_bytes(left * 4));
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 256 * i;
-      const int key = idx >> 3, part = idx & 7;
-      f.kv[i] = buffer_load16(kr, uint32_t(key * a.k_row_stride + part * 16));
+  // Paged keys: the pages of the four 16-key groups of a chunk (each group inside one
+  // page) are read one fetch ahead with one vector load (lane j: group j % 4) and
+  // picked out with readlane, so a fetch never waits on its own block-table lookup;
+  // the load sits ahead of the chunk's K loads in the memory counter's order.
+  int pg_next = 0;
+  auto load_pages = [&](int c) {
+    const int pos = c + 16 * (lane & 3);
+    int pg = 0;
+    if (pos < klim) {
+      const int pi = a.page_shift >= 0 ? pos >> a.page_shift : pos / a.page_size;
+      pg = min(max(a.block_table[pi], 0), a.num_pages - 1);
     }
-    f.ks = buffer_load_f32(sr, uint32_t((tid & (kChunk - 1)) * 4));
+    pg_next = pg;
+  };
+  auto fetch = [&](Fetch &f, int c) {
+    if constexpr (PAGED) {
+      const int p0 = __builtin_amdgcn_readlane(pg_next, 0), p1 = __builtin_amdgcn_readlane(pg_next, 1);
+      const int p2 = __builtin_amdgcn_readlane(pg_next, 2), p3 = __builtin_amdgcn_readlane(pg_next, 3);
+      load_pages(c + kChunk);
+      auto page_of = [&](int grp) { return grp == 0 ? p0 : grp == 1 ? p1 : grp == 2 ? p2 : p3; };
+      auto within = [&](int pos) { return a.page_shift >= 0 ? pos & (a.page_size - 1) : pos % a.page_size; };
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int idx = tid + 256 * i;
+        const int key = idx >> 3, part = idx & 7;
+        const int pos = c + key;
+        f.kv[i] = v4i{0, 0, 0, 0};
+        if (pos < klim)
+          f.kv[i] = load16(a.kbase + int64_t(page_of(key >> 4)) * a.page_stride + within(pos) * 128 + part * 16);
+      }
+      const int key = tid & (kChunk - 1), pos = c + key;
+      f.ks = 0.f;
+      if (pos < klim)
+        f.ks = *reinterpret_cast<const float *>(a.kbase + int64_t(page_of(key >> 4)) * a.page_stride +
+                                                a.page_size * 128 + within(pos) * 4);
+    } else {
+      const int64_t left = max(int64_t(a.N) - c, int64_t(0));
+      const buffer_rsrc kr = make_rsrc(a.k + int64_t(c) * a.k_row_stride, range_bytes(left * a.k_row_stride));
+      const buffer_rsrc sr = make_rsrc(a.k_scale + c, range_bytes(left * 4));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int idx = tid + 256 * i;
+        const int key = idx >> 3, part = idx & 7;
+        f.kv[i] = buffer_load16(kr, uint32_t(key * a.k_row_stride + part * 16));
+      }
+      f.ks = buffer_load_f32(sr, uint32_t((tid & (kChunk - 1)) * 4));
+    }
   };
   auto stage = [&](const Fetch &f, int buf) {
 #pragma unroll
@@ -312,6 +353,7 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
 
   Fetch f[kDepth];
   if (c0 < c_end) {
+    if constexpr (PAGED) load_pages(c0);
     fetch(f[0], c0);
     stage(f[0], 0);
 #pragma unroll
@@ -345,14 +387,25 @@ hipError_t launch_mqa_logits(const MqaArgs &a, int num_cus, hipStream_t stream) 
   splits = (a.N + split_keys - 1) / split_keys;
   const dim3 grid(tiles, splits);
   const int ht = (a.H + 15) / 16;
-  if (ht <= 1)
-    mqa_logits_fp8_kernel<1><<<grid, 256, 0, stream>>>(a, split_keys);
-  else if (ht <= 2)
-    mqa_logits_fp8_kernel<2><<<grid, 256, 0, stream>>>(a, split_keys);
-  else if (ht <= 4)
-    mqa_logits_fp8_kernel<4><<<grid, 256, 0, stream>>>(a, split_keys);
-  else
-    mqa_logits_fp8_kernel<8><<<grid, 256, 0, stream>>>(a, split_keys);
+  if (a.block_table) {
+    if (ht <= 1)
+      mqa_logits_fp8_kernel<1, true><<<grid, 256, 0, stream>>>(a, split_keys);
+    else if (ht <= 2)
+      mqa_logits_fp8_kernel<2, true><<<grid, 256, 0, stream>>>(a, split_keys);
+    else if (ht <= 4)
+      mqa_logits_fp8_kernel<4, true><<<grid, 256, 0, stream>>>(a, split_keys);
+    else
+      mqa_logits_fp8_kernel<8, true><<<grid, 256, 0, stream>>>(a, split_keys);
+  } else {
+    if (ht <= 1)
+      mqa_logits_fp8_kernel<1, false><<<grid, 256, 0, stream>>>(a, split_keys);
+    else if (ht <= 2)
+      mqa_logits_fp8_kernel<2, false><<<grid, 256, 0, stream>>>(a, split_keys);
+    else if (ht <= 4)
+      mqa_logits_fp8_kernel<4, false><<<grid, 256, 0, stream>>>(a, split_keys);
+    else
+      mqa_logits_fp8_kernel<8, false><<<grid, 256, 0, stream>>>(a, split_keys);
+  }
   return hipGetLastError();
 }
 

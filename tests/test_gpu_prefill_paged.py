@@ -2,7 +2,8 @@
 (idx_paged_prefill_logits) against the oracle's paged logits with per-row ends: small
 cases with ragged row ends, odd row counts, head counts that are not a multiple of 16,
 both formats and several page sizes (one not a power of two); the full 8192 x 8192
-MXFP4 chunk on sampled rows; and, for fp8 pages, every row bit for bit against the
+MXFP4 chunk on sampled rows; a full-size fp8 chunk on sampled rows; and, where the
+decode walk serves the chunk (MXFP4, 128 heads), every row bit for bit against the
 decode entry point fed the same rows as two-row sequences."""
 
 import numpy as np
@@ -44,7 +45,7 @@ def _oracle(pi, rows, row_end=None, width=None, magnitude=False):
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
 @pytest.mark.parametrize("M,N,H,P", [(37, 300, 64, 64), (64, 1000, 16, 16), (130, 777, 32, 128), (3, 200, 64, 64),
-                                     (21, 500, 24, 48)])
+                                     (21, 500, 24, 48), (9, 300, 128, 64)])
 def test_paged_prefill_small(fmt, M, N, H, P):
     width = -(-N // 64) * 64 + 32
     wl = workloads.paged_prefill(seed=M + N + P, M=M, N=N, H=H, width=width, topk=16, fmt=fmt, page_size=P)
@@ -72,11 +73,12 @@ def test_paged_prefill_ragged_ends(fmt):
 
 
 def test_paged_prefill_is_the_decode_walk():
-    # fp8 pages: rows 2g, 2g+1 are one walk of the decode kernel over the same pages,
-    # the same bits as idx_paged_mqa_logits with those rows as a two-row (MTP)
-    # sequence (MXFP4 pages take the chunk kernel, whose |x| split sums differently)
-    fmt = "fp8"
-    wl = workloads.paged_prefill(seed=9, M=48, N=700, H=64, width=768, topk=16, fmt=fmt)
+    # MXFP4 pages with 128 heads: rows 2g, 2g+1 are one walk of the decode kernel over
+    # the same pages, the same bits as idx_paged_mqa_logits with those rows as a two-row
+    # (MTP) sequence (fp8 pages and MXFP4 pages with up to 64 heads take the chunk
+    # kernels, whose |x| split sums differently)
+    fmt = "mxfp4"
+    wl = workloads.paged_prefill(seed=9, M=48, N=700, H=128, width=768, topk=16, fmt=fmt)
     pi = _inputs.paged_inputs(wl)
     got = _run(pi).cpu().numpy()
     G = wl.M // 2
@@ -103,3 +105,18 @@ def test_paged_prefill_full_chunk():
     _parity.check_logits(L[rows], want, _oracle(pi, rows, magnitude=True), what="config 6 sampled rows",
                          allow_floor=False)
     np.testing.assert_array_equal(tk[rows], indexer.topk(L[rows], None, wl.row_end[rows], k))
+
+
+def test_paged_prefill_full_chunk_fp8():
+    # the 8192 x 8192 chunk on an fp8 paged cache (the contiguous prefill kernel reading
+    # its keys through the block table): sampled rows against the oracle, every row's
+    # -inf tail
+    wl = workloads.paged_prefill(seed=12, M=8192, N=8192, H=64, width=8192, topk=2048, fmt="fp8")
+    pi = _inputs.paged_inputs(wl)
+    L = _run(pi).cpu().numpy()
+    ends = np.minimum(wl.row_end, wl.width)
+    cols = np.arange(wl.width)
+    assert np.array_equal(np.isneginf(L), cols[None, :] >= ends[:, None])
+    rows = np.array([0, 1, 63, 64, 2047, 4095, 5000, 8190, 8191])
+    _parity.check_logits(L[rows], _oracle(pi, rows), _oracle(pi, rows, magnitude=True), what="fp8 chunk sampled rows",
+                         allow_floor=False)
