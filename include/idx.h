@@ -317,7 +317,7 @@ idx_status idx_topk_to_slots(const int32_t *topk, int64_t topk_row_stride, int32
  *   block_table   [max_blocks] int32: the sequence's pages.
  *   logits        [M, width] fp32 with logits_row_stride (multiple of 4, 16-byte
  *                 aligned); -inf at and past each row's end.
- *   Limits: M >= 0; M * ceil(width / 64) < 2^31; 1 <= H <= 128.
+ *   Limits: 0 <= M <= 16384; M * ceil(width / 64) < 2^31; 1 <= H <= 128.
  */
 idx_status idx_paged_prefill_logits(const idx_paged_cache *cache, const void *q, const int32_t *q_scale,
                                     const float *w, const int32_t *row_end, const int32_t *block_table,
