@@ -283,7 +283,9 @@ def test_paged_prefill_checks(lib):
     assert _pf(os=510) == STRIDE
     assert _pf(q=P + 4) == STRIDE
     assert _pf(H=0) == SHAPE
-    assert _pf(M=2 ** 20, width=2 ** 20) == SHAPE  # more walks than the prefix sums hold
+    assert _pf(M=2 ** 20, width=2 ** 20) == SHAPE  # past the row limit
+    assert _pf(M=16385) == SHAPE  # 16384 rows at most
+    assert _pf(H=129) == SHAPE
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path; a GPU is visible")
