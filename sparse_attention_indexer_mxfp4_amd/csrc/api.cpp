@@ -186,6 +186,7 @@ idx_status idx_paged_prefill_logits(const idx_paged_cache *cache, const void *q,
                                              &empty);
   if (s != IDX_OK || empty) return s;
   if (int64_t(M) * ((int64_t(width) + 63) / 64) > INT32_MAX) return IDX_ERR_SHAPE;
+  if (width == 0) return IDX_OK;  // no column to write
   int cus = 0;
   if ((s = current_device(&cus)) != IDX_OK) return s;
   if (cache->fmt == IDX_KV_MXFP4_E2M1 && H <= 64) {

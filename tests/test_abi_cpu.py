@@ -286,6 +286,7 @@ def test_paged_prefill_checks(lib):
     assert _pf(M=2 ** 20, width=2 ** 20) == SHAPE  # past the row limit
     assert _pf(M=16385) == SHAPE  # 16384 rows at most
     assert _pf(H=129) == SHAPE
+    assert _pf(width=0, out=None) == OK  # nothing to write, nothing launched
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path; a GPU is visible")
