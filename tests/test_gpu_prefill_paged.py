@@ -2,9 +2,10 @@
 (idx_paged_prefill_logits) against the oracle's paged logits with per-row ends: small
 cases with ragged row ends, odd row counts, head counts that are not a multiple of 16,
 both formats and several page sizes (one not a power of two); the full 8192 x 8192
-MXFP4 chunk on sampled rows; a full-size fp8 chunk on sampled rows; and, where the
-decode walk serves the chunk (MXFP4, 128 heads), every row bit for bit against the
-decode entry point fed the same rows as two-row sequences."""
+MXFP4 chunk on sampled rows; a full-size fp8 chunk on sampled rows; fp8 pages bit for
+bit against the contiguous entry point over the same keys laid out contiguously; and,
+where the decode walk serves the chunk (MXFP4, 128 heads), every row bit for bit
+against the decode entry point fed the same rows as two-row sequences."""
 
 import numpy as np
 import pytest
@@ -120,3 +121,19 @@ def test_paged_prefill_full_chunk_fp8():
     rows = np.array([0, 1, 63, 64, 2047, 4095, 5000, 8190, 8191])
     _parity.check_logits(L[rows], _oracle(pi, rows), _oracle(pi, rows, magnitude=True), what="fp8 chunk sampled rows",
                          allow_floor=False)
+
+
+@pytest.mark.parametrize("P,pad", [(64, 16), (16, 0), (48, 32)])
+def test_paged_prefill_fp8_is_the_contiguous_kernel(P, pad):
+    # fp8 pages: the same bits as idx_mqa_logits over the sequence's keys laid out
+    # contiguously, since both calls run the one prefill kernel with the same tiling;
+    # this pins the page lookups and byte offsets of the paged key reads exactly
+    N = 12 * P
+    wl = workloads.paged_prefill(seed=20 + P, M=77, N=N, H=64, width=N, topk=16, fmt="fp8", page_size=P)
+    pi = _inputs.paged_inputs(wl, stride_pad=pad)
+    got = _run(pi).cpu().numpy()
+    ends = np.minimum(wl.row_end, N).astype(np.int32)
+    contig = ops.idx_mqa_logits(_dev(pi.q), _dev(pi.k_codes[:N]), _dev(pi.k_scales[:N]), _dev(wl.w),
+                                _dev(np.zeros(wl.M, np.int32)), _dev(ends))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got, contig.cpu().numpy())
