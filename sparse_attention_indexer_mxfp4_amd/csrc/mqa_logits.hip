@@ -233,31 +233,33 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
   // page) are read one fetch ahead with one vector load (lane j: group j % 4) and
   // picked out with readlane, so a fetch never waits on its own block-table lookup;
   // the load sits ahead of the chunk's K loads in the memory counter's order.
+  // The entry is kept raw (clamped to the pool where it is used) so that nothing waits
+  // on it here; positions past the keys read the last valid entry, which is not used.
   int pg_next = 0;
   auto load_pages = [&](int c) {
-    const int pos = c + 16 * (lane & 3);
-    int pg = 0;
-    if (pos < klim) {
-      const int pi = a.page_shift >= 0 ? pos >> a.page_shift : pos / a.page_size;
-      pg = min(max(a.block_table[pi], 0), a.num_pages - 1);
-    }
-    pg_next = pg;
+    const int pos = min(c + 16 * (lane & 3), klim - 1);
+    pg_next = a.block_table[a.page_shift >= 0 ? pos >> a.page_shift : pos / a.page_size];
   };
   auto fetch = [&](Fetch &f, int c) {
     if constexpr (PAGED) {
-      const int p0 = __builtin_amdgcn_readlane(pg_next, 0), p1 = __builtin_amdgcn_readlane(pg_next, 1);
-      const int p2 = __builtin_amdgcn_readlane(pg_next, 2), p3 = __builtin_amdgcn_readlane(pg_next, 3);
+      auto clamp_page = [&](int pg) { return min(max(pg, 0), a.num_pages - 1); };
+      const int p0 = clamp_page(__builtin_amdgcn_readlane(pg_next, 0));
+      const int p1 = clamp_page(__builtin_amdgcn_readlane(pg_next, 1));
+      const int p2 = clamp_page(__builtin_amdgcn_readlane(pg_next, 2));
+      const int p3 = clamp_page(__builtin_amdgcn_readlane(pg_next, 3));
       load_pages(c + kChunk);
       auto page_of = [&](int grp) { return grp == 0 ? p0 : grp == 1 ? p1 : grp == 2 ? p2 : p3; };
       auto within = [&](int pos) { return a.page_shift >= 0 ? pos & (a.page_size - 1) : pos % a.page_size; };
+      // a wave's 16-byte pieces of load i all lie in one 16-key group, so one page: a
+      // range-checked buffer load over that page's values, keys past the end out of range
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int idx = tid + 256 * i;
         const int key = idx >> 3, part = idx & 7;
         const int pos = c + key;
-        f.kv[i] = v4i{0, 0, 0, 0};
-        if (pos < klim)
-          f.kv[i] = load16(a.kbase + int64_t(page_of(key >> 4)) * a.page_stride + within(pos) * 128 + part * 16);
+        const int grp = uniform(key >> 4);
+        const buffer_rsrc pr = make_rsrc(a.kbase + int64_t(page_of(grp)) * a.page_stride, uint32_t(a.page_size) * 128u);
+        f.kv[i] = buffer_load16(pr, pos < klim ? uint32_t(within(pos) * 128 + part * 16) : 0xFFFFFFF0u);
       }
       const int key = tid & (kChunk - 1), pos = c + key;
       f.ks = 0.f;
