@@ -23,6 +23,7 @@
 // selected bin holds more keys than the list (heavy ties), digit 3 and the per-wave
 // counts come from extra passes over the row instead.
 #include <cstddef>
+#include <mutex>
 
 #include "device.h"
 #include "launch.h"
@@ -710,15 +711,25 @@ hipError_t launch_topk(const TopkArgs &a, int, hipStream_t stream) {
   // LDS instead of three (8192 rows of 8192 keys: top-k 98 -> 86 us).
   const int cap = a.rows >= 1024 ? max(256, ((min(a.width, kMaxCache) / 2) + 255) & ~255) : min(a.width, kMaxCache);
   const size_t lds = size_t((cap + 255) & ~255) * sizeof(uint32_t);  // whole steps of the cached walk
-  static bool lds_raised = false;
-  if (!lds_raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&topk_kernel<1024>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxCache * sizeof(uint32_t)));
+  // the dynamic LDS limit is raised once per device (calls from several threads or
+  // devices serialise on the flag)
+  {
+    constexpr int kDevices = 64;
+    static std::mutex mu;
+    static bool lds_raised[kDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&topk_kernel<256>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxCache * sizeof(uint32_t)));
-    if (e != hipSuccess) return e;
-    lds_raised = true;
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev < 0 || dev >= kDevices || !lds_raised[dev]) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void *>(&topk_kernel<1024>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxCache * sizeof(uint32_t)));
+      if (e != hipSuccess) return e;
+      e = hipFuncSetAttribute(reinterpret_cast<const void *>(&topk_kernel<256>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxCache * sizeof(uint32_t)));
+      if (e != hipSuccess) return e;
+      if (dev >= 0 && dev < kDevices) lds_raised[dev] = true;
+    }
   }
   // few rows: the widest workgroup per row; many rows: narrower ones, more per CU
   if (a.rows >= 1024)
