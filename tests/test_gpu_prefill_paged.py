@@ -137,3 +137,21 @@ def test_paged_prefill_fp8_is_the_contiguous_kernel(P, pad):
                                 _dev(np.zeros(wl.M, np.int32)), _dev(ends))
     torch.cuda.synchronize()
     np.testing.assert_array_equal(got, contig.cpu().numpy())
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("M,N,H,width,P", [(1, 50, 1, 57, 16), (5, 130, 7, 130, 64), (9, 1000, 64, 130, 64),
+                                           (16, 64, 16, 66, 16)])
+def test_paged_prefill_edge_shapes(fmt, M, N, H, width, P):
+    # one row and one head, widths that are not a multiple of 4 or of a chunk, a width
+    # shorter than the sequence (ends clamped to it), an empty first row
+    wl = workloads.paged_prefill(seed=M * 7 + N + width, M=M, N=N, H=H, width=max(width, N), topk=16, fmt=fmt,
+                                 page_size=P)
+    pi = _inputs.paged_inputs(wl)
+    re = wl.row_end.copy()
+    re[0] = 0
+    got = _run(pi, row_end=re, width=width).cpu().numpy()[:, :width]
+    rows = np.arange(M)
+    want = _oracle(pi, rows, row_end=np.minimum(re, width), width=width)
+    _parity.check_logits(got, want, _oracle(pi, rows, row_end=np.minimum(re, width), width=width, magnitude=True),
+                         what=f"edge {fmt} M={M} H={H} width={width}")
