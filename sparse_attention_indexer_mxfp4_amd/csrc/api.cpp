@@ -209,6 +209,7 @@ idx_status idx_paged_prefill_logits(const idx_paged_cache *cache, const void *q,
     a.H = H;
     a.logits = logits;
     a.logits_row_stride = logits_row_stride;
+    a.paged = 1;  // the paged kernel even for an empty table: it then reads nothing
     a.kbase = static_cast<const uint8_t *>(cache->base);
     a.page_stride = cache->page_stride_bytes;
     a.block_table = block_table;

@@ -20,9 +20,11 @@ struct MqaArgs {
   int32_t M, N, H;
   float *logits;
   int64_t logits_row_stride;  // elements
-  // keys straight off an fp8 paged cache (block_table != nullptr; k and k_scale unused):
-  // key s lives in page block_table[s / page_size], keys at or past key_limit are not
-  // read; columns still run over [0, N)
+  // keys straight off an fp8 paged cache (paged != 0; k and k_scale unused): key s
+  // lives in page block_table[s / page_size], keys at or past key_limit are not read
+  // (with key_limit == 0 neither the table nor a page is touched and every column
+  // is -inf); columns still run over [0, N)
+  int32_t paged;
   const uint8_t *kbase;
   int64_t page_stride;  // bytes
   const int32_t *block_table;

@@ -389,7 +389,7 @@ hipError_t launch_mqa_logits(const MqaArgs &a, int num_cus, hipStream_t stream) 
   splits = (a.N + split_keys - 1) / split_keys;
   const dim3 grid(tiles, splits);
   const int ht = (a.H + 15) / 16;
-  if (a.block_table) {
+  if (a.paged) {
     if (ht <= 1)
       mqa_logits_fp8_kernel<1, true><<<grid, 256, 0, stream>>>(a, split_keys);
     else if (ht <= 2)

@@ -290,6 +290,18 @@ def test_paged_prefill_checks(lib):
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path; a GPU is visible")
+def test_paged_prefill_empty_table_passes_host_checks(lib):
+    # an fp8 chunk with no block-table entries (NULL table, max_blocks 0) but rows that
+    # end past 0 is a valid call: every column is -inf. It must pass the host checks and
+    # reach the device query (the GPU test runs it); the kernel chosen for fp8 pages
+    # is then the paged one, which reads neither the table nor a page when no key exists
+    f = lib.idx_paged_prefill_logits
+    c = _cache()
+    assert f(ctypes.byref(c), P, None, P, P, None, 0, 64, 64, P, 512, 512, None) == DEVICE
+    assert f(ctypes.byref(_cache(fmt=1)), P, P, P, P, None, 0, 64, 64, P, 512, 512, None) == DEVICE
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path; a GPU is visible")
 def test_valid_call_without_device_reports_device_error(lib):
     # arguments pass every host check, so the call reaches the device query, which
     # fails here because this machine has no GPU; nothing is launched
