@@ -338,9 +338,12 @@ def idx_q_rope_quant(q: torch.Tensor, fmt: int, positions: torch.Tensor | None, 
 
 
 def idx_topk_to_slots(topk: torch.Tensor, block_table: torch.Tensor, page_size: int, next_n: int = 1,
-                      row_seq: torch.Tensor | None = None, row_valid: torch.Tensor | None = None):
+                      row_seq: torch.Tensor | None = None, row_valid: torch.Tensor | None = None,
+                      slots: torch.Tensor | None = None, indptr: torch.Tensor | None = None,
+                      lens: torch.Tensor | None = None):
     """Top-k rows [rows, k] int32 of local positions -> (slots [rows*k] int32 of which
-    the first indptr[-1] are used, indptr [rows + 1] int32, lens [rows] int32)."""
+    the first indptr[-1] are used, indptr [rows + 1] int32, lens [rows] int32). The
+    three outputs may be passed in (int32, at least those sizes)."""
     _need(topk, torch.int32, "topk")
     _need(block_table, torch.int32, "block_table")
     if topk.dim() != 2 or topk.stride(1) != 1 or block_table.dim() != 2 or block_table.stride(1) != 1:
@@ -351,9 +354,16 @@ def idx_topk_to_slots(topk: torch.Tensor, block_table: torch.Tensor, page_size: 
         _need(row_valid, torch.uint8, "row_valid"); _contig(row_valid, "row_valid")
     rows, k = topk.shape
     dev = topk.device
-    slots = torch.empty(max(rows * k, 1), dtype=torch.int32, device=dev)
-    indptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
-    lens = torch.empty(max(rows, 1), dtype=torch.int32, device=dev)
+    if slots is None:
+        slots = torch.empty(max(rows * k, 1), dtype=torch.int32, device=dev)
+    if indptr is None:
+        indptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    if lens is None:
+        lens = torch.empty(max(rows, 1), dtype=torch.int32, device=dev)
+    for t, n, name in ((slots, rows * k, "slots"), (indptr, rows + 1, "indptr"), (lens, rows, "lens")):
+        _need(t, torch.int32, name); _contig(t, name)
+        if t.numel() < n:
+            raise ValueError(f"{name} holds fewer than {n} entries")
     _abi.check(_abi.lib().idx_topk_to_slots(_ptr(topk), topk.stride(0), rows, k, _ptr(row_seq), next_n,
                                             block_table.shape[0], _ptr(row_valid), _ptr(block_table),
                                             block_table.stride(0), block_table.shape[1], page_size, _ptr(slots),

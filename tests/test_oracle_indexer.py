@@ -47,6 +47,29 @@ def test_handworked_fp8_contiguous():
         assert indexer.topk(out, g["ks"], g["ke"], int(kk)).tolist() == exp
 
 
+def test_handworked_magnitude():
+    # the oracle's magnitude mode (the row scale of the tolerance floor) on a hand-worked
+    # input whose dot products cancel, through the contiguous and the paged routes
+    g = _load("handworked_magnitude.json")
+    q = np.zeros((1, 2, 128), np.uint8)
+    k = np.zeros((2, 128), np.uint8)
+    for e in g["q"]:
+        q[e["row"], e["head"], e["lane"]] = int(e["code"], 16)
+    for e in g["k"]:
+        k[e["key"], e["lane"]] = int(e["code"], 16)
+    ksc, w = np.float32(g["k_scale"]), np.float32(g["w"])
+    got = indexer.mqa_logits_fp8(q, k, ksc, w, g["ks"], g["ke"])
+    mag = indexer.mqa_logits_fp8(q, k, ksc, w, g["ks"], g["ke"], magnitude=True)
+    assert got.tolist() == g["expected_logits"]
+    assert mag.tolist() == g["expected_magnitude"]
+    P = 16
+    pool = np.zeros((1, cache.fp8_page_bytes(P, 128)), np.uint8)
+    cache.store_fp8(pool, [0, 1], k, ksc, P)
+    pmag = indexer.paged_logits(pool, "fp8", P, np.zeros((1, 1), np.int32), [2], q[None], w, 1, 1, 4,
+                                magnitude=True)
+    assert pmag[0, :2].tolist() == g["expected_magnitude"][0] and np.isneginf(pmag[0, 2:]).all()
+
+
 def test_handworked_mxfp4_paged():
     g = _load("handworked_mxfp4_paged.json")
     H, D, P = 2, 128, 64
