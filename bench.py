@@ -1,14 +1,21 @@
 """Indexer benchmark on one MI355X: keys scored per second for one whole indexer step
-(logits over every cached key, causal masks, per-row top-k) on a seeded synthetic
-workload, with the dominant kernel's roofline fraction and the CPU oracle beside it.
+(logits over every cached key, causal masks, per-row top-k) on seeded synthetic
+workloads, with the dominant kernel's roofline fraction and the CPU oracle beside it.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config N] [--headline-only]
+                    [--no-cpu-baseline] [--no-calibration]
 
-Default workload: paged fp8 decode, 32 sequences, context lengths U[1024, 16384], 64
-heads, logits width 32768, top-2048. ``--config 1..5`` selects one of the five
-workloads. Inputs live in HBM before timing starts. Each timed step reads a different
-copy of the K cache (copies totalling more than 512 MB rotate), so the 256 MB
-Infinity Cache cannot hold a step's keys from the previous visit.
+Default: the headline is the paged fp8 MTP decode step (128 sequences x 2 rows,
+context lengths log-uniform on [4096, 65536], 64 heads, logits width 65536,
+top-2048), the largest decode workload; the line also carries the fp8 decode
+(B = 32), the fp8 prefill chunk (8192 x 8192) and the MXFP4 decode (B = 64) as
+sub-objects under "configs", each with its own roofline and CPU oracle baseline, and
+the ceilings measured on this GPU (streaming copy / read, fp8 / fp4 matrix loops)
+under "calibration". ``--config N`` prints one workload's line instead (1-5: the five
+workloads; 6: the MXFP4 prefill chunk read off the paged cache). Inputs live in HBM
+before timing starts. Each timed step reads a different copy of the K cache (copies
+totalling more than 512 MB rotate), so the 256 MB Infinity Cache cannot hold a step's
+keys from the previous visit.
 
 Prints ONE JSON line.
 """
@@ -79,9 +86,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6],
-                   help="1-5: the indexer's five workloads; 6: the MXFP4 prefill chunk read off the paged cache")
+    p.add_argument("--config", type=int, default=None, choices=[1, 2, 3, 4, 5, 6],
+                   help="one workload's line only (1-5: the indexer's five workloads; 6: the MXFP4 prefill chunk "
+                        "read off the paged cache); default: the MTP headline with the others as sub-objects")
+    p.add_argument("--headline-only", action="store_true", help="default mode without the sub-objects")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-calibration", action="store_true", help="skip the measured copy / matrix-core ceilings")
     p.add_argument("--two-level", action="store_true",
                    help="time the two-level indexer on a paged workload instead: the source walk with block "
                         "maxima, the candidate pool, and a consumer that scores only the pool (prints its own "
@@ -238,8 +248,64 @@ def cpu_baseline(cfg, wl, budget_s: float = 10.0):
 
 
 # ------------------------------------------------------------------------------------
+# measured ceilings of this device
+# ------------------------------------------------------------------------------------
+def calibration(torch):
+    """HBM and matrix-core ceilings measured on this GPU with libidx_calib's kernels
+    (include/idx_calib.h): a streaming copy and a streaming read of 2 GiB (above the
+    256 MB Infinity Cache), and the dense 16x16x128 fp8 and fp4 matrix loops, each the
+    median of 5 launches timed with HIP events on the launch stream."""
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_indexer_mxfp4_amd", "libidx_calib.so"))
+    P, SZ, I32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    lib.idx_calib_copy.argtypes = [P, P, SZ, P]
+    lib.idx_calib_read.argtypes = [P, SZ, P, P]
+    lib.idx_calib_mfma.argtypes = [I32, I32, P, ctypes.POINTER(ctypes.c_int64), P]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    nbytes = 2 * 2**30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.empty(8192, dtype=torch.float32, device=dev)
+
+    def timed(fn, reps=5):
+        rc = fn()
+        if rc != 0:
+            raise RuntimeError(f"calibration kernel failed: {rc}")
+        ts = []
+        for _ in range(reps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]))
+        return sorted(ts)[len(ts) // 2] * 1e-3
+
+    t_copy = timed(lambda: lib.idx_calib_copy(src.data_ptr(), dst.data_ptr(), nbytes, s))
+    t_read = timed(lambda: lib.idx_calib_read(src.data_ptr(), nbytes, sink.data_ptr(), s))
+    del src, dst
+    out = {"copy_GBps": round(2 * nbytes / t_copy / 1e9, 1), "read_GBps": round(nbytes / t_read / 1e9, 1),
+           "hbm_spec_GBps": HBM_PEAK_GBS}
+    for fmt, name, spec in ((0, "fp8", FP8_MFMA_PEAK_TFLOPS), (1, "fp4", FP4_MFMA_PEAK_TFLOPS)):
+        flop = ctypes.c_int64(0)
+        t = timed(lambda: lib.idx_calib_mfma(fmt, 4000, sink.data_ptr(), ctypes.byref(flop), s))
+        out[f"{name}_mfma_TFLOPs"] = round(flop.value / t / 1e12, 1)
+        out[f"{name}_mfma_spec_TFLOPs"] = spec
+    out["method"] = ("libidx_calib: 2 GiB streaming copy (bytes read + written) and read, 16-byte loads, 8 "
+                     "workgroups per CU; dense 16x16x128 fp8 / fp4 matrix loops from register operands, 8 waves "
+                     "per CU; median of 5 launches, HIP events")
+    return out
+
+
+# ------------------------------------------------------------------------------------
 # GPU
 # ------------------------------------------------------------------------------------
+SUB_CONFIGS = (2, 4, 5)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -257,181 +323,133 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = args.config
-    wl = workloads.CONFIGS[cfg]() if cfg in workloads.CONFIGS else workloads.EXTRA[cfg]()
-    paged = cfg in (2, 3, 5)
-    if cfg == 6:
-        return prefill_paged_main(args, wl, ops, torch, dev)
+    cfg = 3 if args.config is None else args.config
+    if args.two_level:
+        wl = workloads.CONFIGS[cfg]()
+        st = setup_paged(wl, ops, torch, dev)
+        two_level(args, wl, ops, st["pools"], st["copies"], st["fmt"], st["q"], st["q_scale"], st["w"], st["ctx"],
+                  st["bt"], st["logits"], st["ends"], st["out"], st["logits_call"], st["topk_call"])
+        return
 
-    if paged:
-        fmt = ops.FP8 if wl.fmt == "fp8" else ops.MXFP4
-        pb = ops.page_bytes(fmt, wl.page_size)
-        copies = max(1, int(np.ceil(FLUSH_BYTES / (wl.num_pages * pb))))
-        k_dev = torch.from_numpy(wl.k).to(dev)
-        slots = torch.from_numpy(wl.slot_mapping).to(dev)
-        pools = []
-        for _ in range(copies):
-            pool = torch.zeros((wl.num_pages, pb), dtype=torch.uint8, device=dev)
-            ops.idx_k_store(pool, fmt, wl.page_size, k_dev, slots)  # quantise K with the library's own store
-            pools.append(pool)
-        # K store throughput (boundary op, timed on its own)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        ops.idx_k_store(pools[0], fmt, wl.page_size, k_dev, slots)
-        e1.record()
-        torch.cuda.synchronize()
-        kstore_ms = e0.elapsed_time(e1)
-        del k_dev
-        q, q_scale = ops.idx_q_quant(torch.from_numpy(wl.q.reshape(-1, wl.H, wl.D)).to(dev), fmt)
-        q = q.view(wl.B, wl.next_n, wl.H, -1).contiguous()
-        if q_scale is not None:
-            q_scale = q_scale.view(wl.B, wl.next_n, wl.H).contiguous()
-        w = torch.from_numpy(wl.w).to(dev)
-        ctx = torch.from_numpy(wl.context_lens).to(dev)
-        bt = torch.from_numpy(wl.block_table).to(dev)
-        rows = wl.rows
-        logits = torch.empty((rows, (wl.width + 3) // 4 * 4), dtype=torch.float32, device=dev)[:, :wl.width]
-        ends = torch.empty(rows, dtype=torch.int32, device=dev)
-        out = torch.empty((rows, wl.topk), dtype=torch.int32, device=dev)
-
-        def logits_call(i):
-            ops.idx_paged_mqa_logits(pools[i % copies], fmt, wl.page_size, q, q_scale, w, ctx, bt, wl.width,
-                                     logits=logits, row_end_out=ends)
-
-        def topk_call():
-            ops.idx_topk(logits, None, ends, wl.topk, out=out)
-
-        if args.two_level:
-            two_level(args, wl, ops, pools, copies, fmt, q, q_scale, w, ctx, bt, logits, ends, out, logits_call,
-                      topk_call)
-            return
-        ends_host = None
-    else:
-        fmt = ops.FP8
-        kq = torch.from_numpy(wl.k).to(dev)
-        copies = max(1, int(np.ceil(FLUSH_BYTES / (wl.N * (wl.D + 4)))))
-        qc, _ = ops.idx_q_quant(torch.from_numpy(wl.q).to(dev), fmt)
-        # contiguous K: quantise through a page-size-16 pool and view its bytes back as rows
-        P = 16
-        npages = (wl.N + P - 1) // P
-        kpools = []
-        for _ in range(copies):
-            pool = torch.zeros((npages, P * (wl.D + 4)), dtype=torch.uint8, device=dev)
-            ops.idx_k_store(pool, fmt, P, kq, torch.arange(wl.N, dtype=torch.int64, device=dev))
-            vals = pool[:, : P * wl.D].reshape(npages * P, wl.D)[: wl.N]
-            scal = pool[:, P * wl.D:].contiguous().view(torch.float32).reshape(-1)[: wl.N]
-            kpools.append((vals, scal.contiguous()))
-        kstore_ms = None
-        w = torch.from_numpy(wl.w).to(dev)
-        ks = torch.from_numpy(wl.ks).to(dev)
-        ke = torch.from_numpy(wl.ke).to(dev)
-        logits = torch.empty((wl.M, (wl.N + 3) // 4 * 4), dtype=torch.float32, device=dev)[:, :wl.N]
-        out = torch.empty((wl.M, wl.topk), dtype=torch.int32, device=dev)
-
-        def logits_call(i):
-            vals, scal = kpools[i % copies]
-            ops.idx_mqa_logits(qc, vals, scal, w, ks, ke, logits=logits)
-
-        def topk_call():
-            ops.idx_topk(logits, ks, ke, wl.topk, out=out)
-
-    # warmup
-    for i in range(args.warmup):
-        logits_call(i)
-        topk_call()
-    torch.cuda.synchronize()
-    if paged:
-        ends_host = ends.cpu().numpy()
-        keys, nbytes, flop = paged_work(wl, ends_host)
-    else:
-        keys, nbytes, flop = contig_work(wl)
-
-    stream = torch.cuda.current_stream()
-
-    # (1) per-kernel durations with HIP events on the launch stream: the K launches of
-    # each kernel captured back to back in a HIP graph of their own, one untimed
-    # replay, then one replay between two events (an event pair per launch would cost
-    # as much as a decode launch, and launches enqueued from Python could leave the
-    # GPU idle between kernels)
-    def timed_replay(fn):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(args.steps):
-                fn(i)
-        g.replay()
-        torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record(stream)
-        g.replay()
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[1]) / args.steps
-
-    logits_ms = timed_replay(logits_call)
-    topk_ms = timed_replay(lambda i: topk_call())
-
-    # (2) whole-step throughput: the K timed steps captured in one HIP graph (the
-    # calls neither allocate nor synchronise) and replayed once, so the host's
-    # per-launch cost does not pace the GPU
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(args.steps):
-            logits_call(i)
-            topk_call()
-    graph.replay()  # untimed first replay
-    torch.cuda.synchronize()
-    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    t0 = time.perf_counter()
-    step_ev[0].record(stream)
-    graph.replay()
-    step_ev[1].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    b2b_ms = logits_ms
-    logits_ms = in_step(step_ev[0].elapsed_time(step_ev[1]) / args.steps, topk_ms, b2b_ms)
-
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = keys * args.steps / elapsed
-    if cfg == 4 or cfg == 1:
-        achieved = flop / (logits_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / FP8_MFMA_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic("mqa_logits_fp8_kernel", wl.name),
-                "kernel": "mqa_logits_fp8_kernel", "kernel_ms": round(logits_ms, 4),
-                "algorithmic_flop": flop, "algorithmic_bytes": nbytes}
-    else:
-        achieved = nbytes / (logits_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic("paged_logits_kernel", wl.name), "kernel": "paged_logits_kernel",
-                "kernel_ms": round(logits_ms, 4), "algorithmic_bytes": nbytes, "algorithmic_flop": flop}
+    head = measure(cfg, args, ops, workloads, torch, dev, cpu_budget=10.0, one_thread_budget=4.0)
     result = {
         "metric": "indexer keys scored/sec + decode HBM GB/s (% of peak), 1 MI355X",
-        "value": round(value, 1),
+        "value": head["value"],
         "unit": "keys/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if wl_fmt(wl, cfg) == "fp8" else "fp4",
+        "dtype": head["dtype"],
         "data": "synthetic",
-        "config": {"workload": wl.name, "config": cfg, "keys_per_step": keys, "topk": wl.topk,
-                   "timing": TIMING, "logits_ms": round(logits_ms, 4), "logits_b2b_ms": round(b2b_ms, 4),
-                   "topk_ms": round(topk_ms, 4),
-                   "kstore_ms": None if kstore_ms is None else round(kstore_ms, 4), "k_cache_copies": copies},
-        "roofline": roof,
+        "config": head["config"],
+        "roofline": head["roofline"],
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, wl)
+    if "cpu_baseline" in head:
+        result["cpu_baseline"] = head["cpu_baseline"]
+    if args.config is None and not args.headline_only:
+        subs = {}
+        for c in SUB_CONFIGS:
+            torch.cuda.empty_cache()
+            subs[str(c)] = measure(c, args, ops, workloads, torch, dev, cpu_budget=5.0, one_thread_budget=0.0)
+        result["configs"] = subs
+    if not args.no_calibration:
+        torch.cuda.empty_cache()
+        cal = calibration(torch)
+        result["calibration"] = cal
+        for part in [result] + list(result.get("configs", {}).values()):
+            roof = part["roofline"]
+            if roof["bound"] == "hbm":
+                roof["measured_ceiling"] = cal["read_GBps"]
+            else:
+                roof["measured_ceiling"] = cal["fp8_mfma_TFLOPs" if roof["peak"] == FP8_MFMA_PEAK_TFLOPS
+                                              else "fp4_mfma_TFLOPs"]
+            roof["frac_of_measured_ceiling"] = round(roof["achieved"] / roof["measured_ceiling"], 4)
     print(json.dumps(result), flush=True)
 
 
-def prefill_paged_main(args, wl, ops, torch, dev):
-    """The prefill chunk read straight off the paged MXFP4 cache: logits + top-k per step."""
-    fmt = ops.MXFP4
+def setup_paged(wl, ops, torch, dev):
+    """Device inputs of a paged step: K-cache copies quantised by the library's own K
+    store (copies totalling more than FLUSH_BYTES rotate), queries, weights, lengths,
+    block table, and the logits / row-end / top-k outputs, with the two calls."""
+    fmt = ops.FP8 if wl.fmt == "fp8" else ops.MXFP4
+    pb = ops.page_bytes(fmt, wl.page_size)
+    copies = max(1, int(np.ceil(FLUSH_BYTES / (wl.num_pages * pb))))
+    k_dev = torch.from_numpy(wl.k).to(dev)
+    slots = torch.from_numpy(wl.slot_mapping).to(dev)
+    pools = []
+    for _ in range(copies):
+        pool = torch.zeros((wl.num_pages, pb), dtype=torch.uint8, device=dev)
+        ops.idx_k_store(pool, fmt, wl.page_size, k_dev, slots)
+        pools.append(pool)
+    # K store throughput (boundary op, timed on its own)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    ops.idx_k_store(pools[0], fmt, wl.page_size, k_dev, slots)
+    e1.record()
+    torch.cuda.synchronize()
+    kstore_ms = e0.elapsed_time(e1)
+    del k_dev
+    q, q_scale = ops.idx_q_quant(torch.from_numpy(wl.q.reshape(-1, wl.H, wl.D)).to(dev), fmt)
+    q = q.view(wl.B, wl.next_n, wl.H, -1).contiguous()
+    if q_scale is not None:
+        q_scale = q_scale.view(wl.B, wl.next_n, wl.H).contiguous()
+    w = torch.from_numpy(wl.w).to(dev)
+    ctx = torch.from_numpy(wl.context_lens).to(dev)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    rows = wl.rows
+    logits = torch.empty((rows, (wl.width + 3) // 4 * 4), dtype=torch.float32, device=dev)[:, :wl.width]
+    ends = torch.empty(rows, dtype=torch.int32, device=dev)
+    out = torch.empty((rows, wl.topk), dtype=torch.int32, device=dev)
+
+    def logits_call(i):
+        ops.idx_paged_mqa_logits(pools[i % copies], fmt, wl.page_size, q, q_scale, w, ctx, bt, wl.width,
+                                 logits=logits, row_end_out=ends)
+
+    def topk_call(i):
+        ops.idx_topk(logits, None, ends, wl.topk, out=out)
+
+    return dict(fmt=fmt, pools=pools, copies=copies, q=q, q_scale=q_scale, w=w, ctx=ctx, bt=bt, logits=logits,
+                ends=ends, out=out, logits_call=logits_call, topk_call=topk_call, kstore_ms=kstore_ms)
+
+
+def setup_contig(wl, ops, torch, dev):
+    fmt = ops.FP8
+    kq = torch.from_numpy(wl.k).to(dev)
+    copies = max(1, int(np.ceil(FLUSH_BYTES / (wl.N * (wl.D + 4)))))
+    qc, _ = ops.idx_q_quant(torch.from_numpy(wl.q).to(dev), fmt)
+    # contiguous K: quantise through a page-size-16 pool and view its bytes back as rows
+    P = 16
+    npages = (wl.N + P - 1) // P
+    kpools = []
+    for _ in range(copies):
+        pool = torch.zeros((npages, P * (wl.D + 4)), dtype=torch.uint8, device=dev)
+        ops.idx_k_store(pool, fmt, P, kq, torch.arange(wl.N, dtype=torch.int64, device=dev))
+        vals = pool[:, : P * wl.D].reshape(npages * P, wl.D)[: wl.N]
+        scal = pool[:, P * wl.D:].contiguous().view(torch.float32).reshape(-1)[: wl.N]
+        kpools.append((vals, scal.contiguous()))
+    w = torch.from_numpy(wl.w).to(dev)
+    ks = torch.from_numpy(wl.ks).to(dev)
+    ke = torch.from_numpy(wl.ke).to(dev)
+    logits = torch.empty((wl.M, (wl.N + 3) // 4 * 4), dtype=torch.float32, device=dev)[:, :wl.N]
+    out = torch.empty((wl.M, wl.topk), dtype=torch.int32, device=dev)
+
+    def logits_call(i):
+        vals, scal = kpools[i % copies]
+        ops.idx_mqa_logits(qc, vals, scal, w, ks, ke, logits=logits)
+
+    def topk_call(i):
+        ops.idx_topk(logits, ks, ke, wl.topk, out=out)
+
+    return dict(copies=copies, logits_call=logits_call, topk_call=topk_call, kstore_ms=None)
+
+
+def setup_prefill_paged(wl, ops, torch, dev):
+    """The prefill chunk read straight off the paged cache (config 6: MXFP4)."""
+    fmt = ops.FP8 if wl.fmt == "fp8" else ops.MXFP4
     pb = ops.page_bytes(fmt, wl.page_size)
     copies = max(1, int(np.ceil(FLUSH_BYTES / (wl.num_pages * pb))))
     k_dev = torch.from_numpy(wl.k).to(dev)
@@ -456,56 +474,122 @@ def prefill_paged_main(args, wl, ops, torch, dev):
     def topk_call(i):
         ops.idx_topk(logits, None, ends, wl.topk, out=out)
 
+    return dict(copies=copies, logits_call=logits_call, topk_call=topk_call, kstore_ms=None, ends=ends)
+
+
+def measure(cfg, args, ops, workloads, torch, dev, cpu_budget, one_thread_budget):
+    """One workload: K steps (logits + top-k) in one HIP graph timed with HIP events on
+    the launch stream, the two kernels' back-to-back times, the dominant kernel's
+    roofline and the CPU oracle on a bounded sample. Returns the workload's part of
+    the JSON line."""
+    wl = workloads.CONFIGS[cfg]() if cfg in workloads.CONFIGS else workloads.EXTRA[cfg]()
+    paged = cfg in (2, 3, 5)
+    if paged:
+        st = setup_paged(wl, ops, torch, dev)
+    elif cfg == 6:
+        st = setup_prefill_paged(wl, ops, torch, dev)
+    else:
+        st = setup_contig(wl, ops, torch, dev)
+    logits_call, topk_call = st["logits_call"], st["topk_call"]
+
     for i in range(args.warmup):
         logits_call(i)
         topk_call(i)
     torch.cuda.synchronize()
-    keys, nbytes, flop = prefill_paged_work(wl)
-    logits_ms = timed_graph(torch, logits_call, args.steps)
+    if paged:
+        keys, nbytes, flop = paged_work(wl, st["ends"].cpu().numpy())
+    elif cfg == 6:
+        keys, nbytes, flop = prefill_paged_work(wl)
+    else:
+        keys, nbytes, flop = contig_work(wl)
+
+    # per-kernel durations: K launches of one kernel back to back in a HIP graph of
+    # their own, one untimed replay, then one replay between two HIP events
+    b2b_ms = timed_graph(torch, logits_call, args.steps)
     topk_ms = timed_graph(torch, topk_call, args.steps)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+
+    # whole-step throughput: the K timed steps captured in one HIP graph (the calls
+    # neither allocate nor synchronise) and replayed once, so the host's per-launch
+    # cost does not pace the GPU
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
         for i in range(args.steps):
             logits_call(i)
             topk_call(i)
-    g.replay()
+    graph.replay()  # untimed first replay
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     t0 = time.perf_counter()
     step_ev[0].record(stream)
-    g.replay()
+    graph.replay()
     step_ev[1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    b2b_ms = logits_ms
-    logits_ms = in_step(step_ev[0].elapsed_time(step_ev[1]) / args.steps, topk_ms, b2b_ms)
-    achieved = flop / (logits_ms * 1e-3) / 1e12
-    result = {
-        "metric": "indexer keys scored/sec, prefill chunk off the paged MXFP4 cache, 1 MI355X",
+    step_ms = step_ev[0].elapsed_time(step_ev[1]) / args.steps
+    logits_ms = in_step(step_ms, topk_ms, b2b_ms)
+    del graph
+
+    fmt = wl_fmt(wl, cfg)
+    if cfg in (1, 4, 6):
+        kernel = "mqa_logits_fp8_kernel" if cfg != 6 else "paged_prefill_fp4_kernel"
+        peak = FP8_MFMA_PEAK_TFLOPS if fmt == "fp8" else FP4_MFMA_PEAK_TFLOPS
+        achieved = flop / (logits_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(kernel, wl.name),
+                "kernel": kernel, "kernel_ms": round(logits_ms, 4),
+                "frac_b2b": round(flop / (b2b_ms * 1e-3) / 1e12 / peak, 4), "kernel_ms_b2b": round(b2b_ms, 4),
+                "algorithmic_flop": flop, "algorithmic_bytes": nbytes}
+    else:
+        achieved = nbytes / (logits_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic("paged_logits_kernel", wl.name), "kernel": "paged_logits_kernel",
+                "kernel_ms": round(logits_ms, 4),
+                "frac_b2b": round(nbytes / (b2b_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "kernel_ms_b2b": round(b2b_ms, 4), "algorithmic_bytes": nbytes, "algorithmic_flop": flop}
+    part = {
         "value": round(keys * args.steps / elapsed, 1),
         "unit": "keys/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp4",
-        "data": "synthetic",
-        "config": {"workload": wl.name, "config": 6, "keys_per_step": keys, "topk": wl.topk,
-                   "timing": TIMING, "logits_ms": round(logits_ms, 4), "logits_b2b_ms": round(b2b_ms, 4),
-                   "topk_ms": round(topk_ms, 4), "k_cache_copies": copies},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP4_MFMA_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / FP4_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("paged_prefill_fp4_kernel", wl.name),
-                     "kernel": "paged_prefill_fp4_kernel", "kernel_ms": round(logits_ms, 4),
-                     "algorithmic_flop": flop, "algorithmic_bytes": nbytes},
+        "dtype": "fp8" if fmt == "fp8" else "fp4",
+        "config": {"workload": wl.name, "config": cfg, "keys_per_step": keys, "topk": wl.topk, "timing": TIMING,
+                   "step_ms": round(step_ms, 4), "logits_ms": round(logits_ms, 4), "logits_b2b_ms": round(b2b_ms, 4),
+                   "topk_ms": round(topk_ms, 4),
+                   "kstore_ms": None if st["kstore_ms"] is None else round(st["kstore_ms"], 4),
+                   "k_cache_copies": st["copies"]},
+        "roofline": roof,
     }
+    del st
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(6, wl, budget_s=5.0)
-    print(json.dumps(result), flush=True)
+        cb = cpu_baseline(cfg, wl, budget_s=cpu_budget)
+        cb["cpu_model"] = cpu_model()
+        if one_thread_budget > 0:
+            try:
+                import threadpoolctl
+
+                with threadpoolctl.threadpool_limits(limits=1):
+                    one = cpu_baseline(cfg, wl, budget_s=one_thread_budget)
+                cb["one_thread"] = {"value": one["value"], "unit": "keys/s", "cores": 1, "sample": one["sample"],
+                                    "seconds": one["seconds"]}
+            except ImportError:
+                pass
+        part["cpu_baseline"] = cb
+    return part
+
+
+def cpu_model():
+    """The host CPU's model name (what lscpu reports as "Model name")."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
 
 
 TIMING = ("K steps in one HIP graph, timed with HIP events on the launch stream; top-k time from HIP events "
@@ -593,7 +677,7 @@ def two_level(args, wl, ops, pools, copies, fmt, q, q_scale, w, ctx, bt, logits,
     dense_keys, _, _ = paged_work(wl, e)
 
     t = {name: timed_graph(torch, fn, args.steps) for name, fn in
-         (("dense_logits", logits_call), ("dense_topk", lambda i: topk_call()), ("source", source),
+         (("dense_logits", logits_call), ("dense_topk", topk_call), ("source", source),
           ("select", select), ("gather", gather), ("pool_topk", pool_topk), ("remap", remap))}
 
     def consumer(i):

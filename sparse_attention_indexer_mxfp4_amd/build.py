@@ -1,9 +1,10 @@
-"""Build libidx.so (the indexer's C ABI and its gfx950 HIP kernels) in-tree with hipcc.
+"""Build libidx.so (the indexer's C ABI and its gfx950 HIP kernels) and libidx_calib.so
+(the measurement kernels of include/idx_calib.h) in-tree with hipcc.
 
 Every HIP source compiles for gfx950 only, with packed-fp32 instruction selection
 disabled (``-Xclang -target-feature -Xclang -packed-fp32-ops``; hipcc's host pass
 warns that it does not know the feature, which is harmless). Objects go to
-``_build/`` next to this file and the library to ``libidx.so`` beside it.
+``_build/`` next to this file and the libraries beside it.
 
     python -m sparse_attention_indexer_mxfp4_amd.build [-v]
 """
@@ -20,6 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libidx.so")
+CALIB_SRC = os.path.join(CSRC, "calib", "calib.hip")
+CALIB_LIB = os.path.join(PKG, "libidx_calib.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 ARCH = "gfx950"
@@ -44,23 +47,31 @@ def _compile(src: str, extra: list[str]) -> tuple[str, str]:
     return obj, r.stderr
 
 
+def _link(objs: list[str], lib: str) -> None:
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
 def build(verbose: bool = False, extra: list[str] | None = None, jobs: int = 8) -> str:
-    """Compile every source and link libidx.so; returns its path. Always rebuilds."""
+    """Compile every source and link libidx.so and libidx_calib.so; returns libidx.so's
+    path. Always rebuilds."""
     os.makedirs(BUILD, exist_ok=True)
     extra = list(extra or [])
+    srcs = sources() + [CALIB_SRC]
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(lambda s: _compile(s, extra), sources()))
+        results = list(ex.map(lambda s: _compile(s, extra), srcs))
     if verbose:
         for obj, err in results:
             noise = [ln for ln in err.splitlines() if "packed-fp32-ops" not in ln]
             if noise:
                 print(obj, "\n".join(noise), file=sys.stderr)
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *[o for o, _ in results], "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    objs = [o for o, _ in results]
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], CALIB_LIB)
     return LIB
 
 

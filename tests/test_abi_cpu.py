@@ -36,6 +36,22 @@ def test_exports_every_declared_function(lib):
     assert sorted(names) == sorted(_abi.EXPORTS)
 
 
+def test_calibration_library_exports():
+    # the measurement kernels bench.py reports beside the spec peaks (include/idx_calib.h)
+    text = open(os.path.join(ROOT, "include", "idx_calib.h")).read()
+    names = sorted(set(re.findall(r"^\s*int32_t\s+(idx_calib_\w+)\s*\(", text, re.M)))
+    assert names == ["idx_calib_copy", "idx_calib_mfma", "idx_calib_mfma_sink_words", "idx_calib_read",
+                     "idx_calib_read_sink_words"]
+    calib = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_indexer_mxfp4_amd", "libidx_calib.so"))
+    for name in names:
+        assert hasattr(calib, name), name
+    assert calib.idx_calib_read_sink_words() == 8192 and calib.idx_calib_mfma_sink_words() == 8192
+    # argument checks come before any device call
+    calib.idx_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert calib.idx_calib_copy(P, P, 15, None) != 0
+    assert calib.idx_calib_copy(None, P, 16, None) != 0
+
+
 def test_version_and_status_text(lib):
     assert lib.idx_abi_version() == 1
     for s in range(8):

@@ -45,9 +45,11 @@ def same(got, want, what):
     assert np.array_equal(g, w), f"{what}: values differ from the unpadded call"
 
 
-def _paged(fmt, next_n=2, width=1101, H=64):
+def _paged(fmt, next_n=2, H=64):
+    # a call may pass a width below the context (rows are cut at the width); the
+    # workload itself is drawn at the longest width used here
     lens = np.array([0, 1, 63, 65, 300, 1000, 7])
-    wl = workloads.paged(seed=40 + next_n, B=len(lens), next_n=next_n, H=H, ctx_lo=0, ctx_hi=0, width=width,
+    wl = workloads.paged(seed=40 + next_n, B=len(lens), next_n=next_n, H=H, ctx_lo=0, ctx_hi=0, width=1101,
                          topk=33, fmt=fmt, context_lens=lens)
     pi = _inputs.paged_inputs(wl, stride_pad=16)
     f = ops.FP8 if fmt == "fp8" else ops.MXFP4
@@ -73,7 +75,7 @@ def test_guard_mqa_logits():
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
 @pytest.mark.parametrize("next_n,width", [(1, 1101), (2, 1101), (2, 65), (3, 258)])
 def test_guard_paged_logits_and_block_max(fmt, next_n, width):
-    wl, args = _paged(fmt, next_n, width)
+    wl, args = _paged(fmt, next_n)
     rows = wl.rows
     buf, view = guarded(rows, width)
     ebuf, ends = guarded(1, rows, torch.int32)
@@ -155,7 +157,7 @@ def test_guard_topk_to_slots():
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
 def test_guard_two_level(fmt):
     width, block, n_cand, k = 1101, 32, 7, 40
-    wl, args = _paged(fmt, 2, width)
+    wl, args = _paged(fmt, 2)
     rows = wl.rows
     logits, ends, bm = ops.idx_paged_mqa_logits_block_max(*args, width, block)
     # the pool: guarded output, then unpadded
