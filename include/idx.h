@@ -174,13 +174,31 @@ size_t idx_paged_mqa_logits_workspace(int32_t B, int32_t next_n, int32_t H, cons
  *              logits, as column - start, in ascending column order, then -1 up to
  *              k entries. Ties at the k-th value go to the lowest column; -0.0 and
  *              +0.0 compare equal. NaN logits are not supported.
- *   workspace  at least idx_topk_workspace() bytes (NULL when that is 0).
+ *   workspace  at least idx_topk_workspace(rows, width, k) bytes of device memory,
+ *              ZERO-FILLED before its first use; every call leaves it zero-filled
+ *              again, so one buffer serves any number of calls. Calls that share a
+ *              workspace must not overlap (issue them on one stream). NULL is allowed
+ *              when the query returns 0 (more than 256 rows).
+ *              With up to 256 rows of more than 65536 columns, 16-byte aligned rows
+ *              (logits and a row stride that is a multiple of 4) and rows * width
+ *              below 2^30, several workgroups share each row: the page treats few rows
+ *              and many rows as different regimes, and one workgroup per long row
+ *              would leave most of the device idle while it walks its row. The workgroups of a row meet at counters in the
+ *              workspace; all of them are resident at once (the grid is sized from the
+ *              device's occupancy), and every wait is bounded: should another kernel
+ *              keep them from being resident for about a second, the call still
+ *              returns but its output is unspecified. Otherwise one workgroup per row.
+ *              The workspace is laid out as 2048 records of 16 bytes (one per
+ *              workgroup) followed by one 36928-byte record per row.
  *   Limits: 1 <= k <= 65536, rows >= 0, width >= 0.
  */
 idx_status idx_topk(const float *logits, int64_t logits_row_stride, int32_t rows, int32_t width,
                     const int32_t *row_start, const int32_t *row_end, int32_t k, int32_t *out,
                     int64_t out_row_stride, void *workspace, size_t workspace_bytes, hipStream_t stream);
+/* Bytes of workspace idx_topk needs: 2048 * 16 + rows * 36928 for 1 <= rows <= 256,
+ * else 0. */
 size_t idx_topk_workspace(int32_t rows, int32_t width, int32_t k);
+
 
 /*
  * idx_k_store - quantise key rows and write them into their cache slots.

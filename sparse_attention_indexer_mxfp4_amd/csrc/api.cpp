@@ -251,7 +251,7 @@ idx_status idx_candidate_blocks(const float *block_max, int64_t block_max_row_st
   if ((s = current_device(&cus)) != IDX_OK) return s;
   idx::TopkArgs a{block_max, block_max_row_stride, rows, num_blocks, nullptr, row_end, n_cand, cand_out,
                   cand_row_stride, block_size};
-  return launched(idx::launch_topk(a, cus, stream));
+  return launched(idx::launch_topk(a, cus, workspace, workspace_bytes, stream));
 }
 
 idx_status idx_apply_candidate_mask(float *logits, int64_t logits_row_stride, int32_t rows, int32_t width,
@@ -295,7 +295,7 @@ idx_status idx_topk(const float *logits, int64_t logits_row_stride, int32_t rows
   int cus = 0;
   if ((s = current_device(&cus)) != IDX_OK) return s;
   idx::TopkArgs a{logits, logits_row_stride, rows, width, row_start, row_end, k, out, out_row_stride, 1};
-  return launched(idx::launch_topk(a, cus, stream));
+  return launched(idx::launch_topk(a, cus, workspace, workspace_bytes, stream));
 }
 
 idx_status idx_k_store(const idx_paged_cache *cache, const void *k, int32_t k_dtype, int64_t k_row_stride,

@@ -161,6 +161,125 @@ __device__ __forceinline__ v8i zero8() {
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// -inf into row[from, to) by one wavefront (lane = lane index), 16-byte streaming
+// stores; `from` is a multiple of 4 and the row is 16-byte aligned.
+__device__ __forceinline__ void fill_neg_inf(float *row, int from, int to, int lane) {
+  const float ninf = neg_inf();
+  for (int c = from + 4 * lane; c < to; c += 256) {
+    if (c + 4 <= to) {
+      __builtin_nontemporal_store(v4f{ninf, ninf, ninf, ninf}, reinterpret_cast<v4f *>(row + c));
+    } else {
+      for (int i = 0; i < 4 && c + i < to; ++i) __builtin_nontemporal_store(ninf, row + c + i);
+    }
+  }
+}
+
+// One step of a reduce-scatter over the 16 lanes of a DPP row. x[0..2*HALF) holds
+// partial sums; the DPP control pairs each lane with one that differs in the bit
+// `upper` tests (and possibly lower bits). The lane keeps the half selected by that
+// bit, adds the partner's copy of the same half, and on return x[0..HALF) holds it.
+template <int CTRL, int HALF>
+__device__ __forceinline__ void reduce_scatter_step(float (&x)[32], bool upper) {
+#pragma unroll
+  for (int j = 0; j < HALF; ++j) {
+    const float keep = upper ? x[j + HALF] : x[j];
+    const float send = upper ? x[j] : x[j + HALF];
+    x[j] = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), CTRL, 0xF, 0xF, false));
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Integer scans and radix-select helpers (top-k).
+// ---------------------------------------------------------------------------------
+
+// Order-preserving 32-bit key of a float: larger float, larger key; -0.0 ranks with
+// +0.0. The smallest key of a non-NaN float is that of -inf (0x007FFFFF), so 0 can
+// stand for "no key".
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// number of set bits of mask below this lane
+__device__ __forceinline__ int lane_prefix(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS traffic): shifts of
+// 1, 2, 4 and 8 lanes inside each 16-lane row, then the last lane of rows 0 and 2
+// broadcast into rows 1 and 3, and lane 31 into rows 2 and 3. Lanes a move does not
+// reach add 0.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum(int x) { return __builtin_amdgcn_readlane(wave_incl_scan(x), 63); }
+
+// Exclusive prefix sum of one value per thread over a workgroup of NT threads;
+// returns the thread's offset and the workgroup total in *total. `scratch` holds
+// NT / 64 ints of LDS. Contains one barrier; callers barrier again before reusing
+// scratch.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int *scratch, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int x = wave_incl_scan(v);
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int t = scratch[w];
+    if (w < wave) before += t;
+    all += t;
+  }
+  *total = all;
+  return before + x - v;
+}
+
+// Radix-select step: wave 0 finds the bin d of hist[0..NBINS) holding the kr-th
+// largest key (larger bin = larger key), i.e. (keys in bins above d) < kr <= (keys in
+// bins at or above d), and stores d in sel[0] and the count above it in sel[1]; the
+// caller synchronises before reading them. Two parallel steps, no serial walk: each
+// lane sums its NBINS/64 bins and a lane scan with a ballot names the lane whose bins
+// hold the kr-th key; then NBINS/64 lanes take one of that lane's bins each (highest
+// first), and a second scan and ballot name the bin.
+template <int NBINS>
+__device__ __forceinline__ void select_bin(const uint32_t *hist, int kr, int *sel) {
+  static_assert(NBINS % 256 == 0, "whole 16-byte loads per lane");
+  constexpr int kPer = NBINS / 64;
+  if ((threadIdx.x >> 6) == 0) {
+    const int lane = threadIdx.x & 63;
+    const int first = NBINS - (lane + 1) * kPer;  // this lane: bins [first, first + kPer), lane 0 highest
+    int local = 0;
+#pragma unroll
+    for (int q = 0; q < kPer / 4; ++q) {
+      const v4i x = *reinterpret_cast<const v4i *>(hist + first + 4 * q);
+      local += (x[0] + x[1]) + (x[2] + x[3]);
+    }
+    const int incl = wave_incl_scan(local);
+    const int run = incl - local;
+    const uint64_t hit = __ballot(run < kr && incl >= kr);
+    const int t = hit ? __builtin_ctzll(hit) : 0;  // one lane when 1 <= kr <= total
+    const int run_t = __builtin_amdgcn_readlane(run, t);
+    const int first_t = NBINS - (t + 1) * kPer;
+    const int v = lane < kPer ? int(hist[first_t + kPer - 1 - lane]) : 0;
+    const int iv = wave_incl_scan(v);
+    const uint64_t hit2 = __ballot(lane < kPer && run_t + iv >= kr);
+    const int j = hit2 ? __builtin_ctzll(hit2) : 0;
+    if (lane == j) {
+      sel[0] = first_t + kPer - 1 - j;
+      sel[1] = run_t + iv - v;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------
 // Encoders of the K store and the query quantiser. Integer-exact, so they agree
 // bit for bit with any other correct implementation of the same rounding.

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "validate.h"
+
 namespace idx {
 
 struct MqaArgs {
@@ -160,7 +162,14 @@ hipError_t launch_paged_logits(const PagedArgs &a, int num_cus, hipStream_t stre
 // a prefill chunk of one sequence off its MXFP4 pages: rows a.B, row ends in
 // a.context_lens, the sequence's pages in a.block_table; H <= 64
 hipError_t launch_paged_prefill_fp4(const PagedArgs &a, int num_cus, hipStream_t stream);
-hipError_t launch_topk(const TopkArgs &a, int num_cus, hipStream_t stream);
+// Per-row top-k. With a scratch buffer of at least topk_scratch_bytes(rows) bytes (zero
+// before the first call; every call leaves it zero) and few rows, several workgroups
+// share each row (topk_coop.hip); otherwise one workgroup per row (topk.hip).
+hipError_t launch_topk(const TopkArgs &a, int num_cus, void *scratch, size_t scratch_bytes, hipStream_t stream);
+
+int topk_coop_grid(int num_cus, int rows, int width);  // its grid for these rows (0: cannot run)
+hipError_t launch_topk_coop(const TopkArgs &a, void *scratch, int grid, hipStream_t stream);
+
 hipError_t launch_k_store(const KStoreArgs &a, hipStream_t stream);
 hipError_t launch_q_quant(const QQuantArgs &a, hipStream_t stream);
 hipError_t launch_q_rope_quant(const QRopeArgs &a, hipStream_t stream);

@@ -50,32 +50,6 @@ constexpr int kChunk = 64;
 constexpr int kDepth = 2;  // K chunks requested ahead of the one being scored
 constexpr int kKeyStride = 144;  // LDS bytes per key / query row: 128 + 16 of padding against bank conflicts
 
-// -inf into row[from, to); `from` is a multiple of 4 and the row is 16-byte aligned.
-__device__ void fill_neg_inf(float *row, int from, int to, int lane) {
-  const float ninf = neg_inf();
-  for (int c = from + 4 * lane; c < to; c += 256) {
-    if (c + 4 <= to) {
-      __builtin_nontemporal_store(v4f{ninf, ninf, ninf, ninf}, reinterpret_cast<v4f *>(row + c));
-    } else {
-      for (int i = 0; i < 4 && c + i < to; ++i) __builtin_nontemporal_store(ninf, row + c + i);
-    }
-  }
-}
-
-// One step of a reduce-scatter over the 16 lanes of a DPP row. x[0..2*HALF) holds
-// partial sums; the DPP control pairs each lane with one that differs in the bit
-// `upper` tests (and possibly lower bits). The lane keeps the half selected by that
-// bit, adds the partner's copy of the same half, and on return x[0..HALF) holds it.
-template <int CTRL, int HALF>
-__device__ __forceinline__ void reduce_scatter_step(float (&x)[32], bool upper) {
-#pragma unroll
-  for (int j = 0; j < HALF; ++j) {
-    const float keep = upper ? x[j + HALF] : x[j];
-    const float send = upper ? x[j] : x[j + HALF];
-    x[j] = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), CTRL, 0xF, 0xF, false));
-  }
-}
-
 template <int HT, bool PAGED>
 __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int split_keys) {
   __shared__ __attribute__((aligned(16))) uint8_t sk[2][kChunk * kKeyStride];

@@ -69,29 +69,6 @@ template <int FMT, int NR>
 constexpr int ring_depth() { return NR == 1 ? 2 : 3; }
 constexpr int kTileStride = 144;  // LDS bytes per key row of a wave's fp8 tile (128 + 16 against bank conflicts)
 
-// Exclusive prefix sum of per-thread values over the workgroup; returns the
-// thread's offset and stores the total in *total.
-__device__ int block_exclusive_scan(int v, int *scratch, int *total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) scratch[wave] = x;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
-    const int t = scratch[w];
-    if (w < wave) before += t;
-    all += t;
-  }
-  *total = all;
-  return before + x - v;
-}
-
 // largest b in [0, B) with pref[b] <= u (pref[B] > u)
 __device__ __forceinline__ int find_seq(const int *pref, int B, int u) {
   int lo = 0, hi = B;
@@ -215,7 +192,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 
     mine += (len + kChunk - 1) / kChunk;
   }
   int total = 0;
-  int run = block_exclusive_scan(mine, s_scan, &total);
+  int run = block_excl_scan<kThreads>(mine, s_scan, &total);
   for (int b = b_lo; b < b_hi; ++b) {
     s_pref[b] = run;
     run += (s_len[b] + kChunk - 1) / kChunk;

@@ -44,32 +44,6 @@ constexpr int kChunk = 64;
 constexpr int kDepth = 2;  // chunks requested ahead of the one being scored
 constexpr int kQtStride = 144;  // LDS bytes per qt A-operand row (128 + 16 against bank conflicts)
 
-// -inf into row[from, to); `from` is a multiple of 4 and the row is 16-byte aligned.
-__device__ void fill_ninf(float *row, int from, int to, int lane) {
-  const float ninf = neg_inf();
-  for (int c = from + 4 * lane; c < to; c += 256) {
-    if (c + 4 <= to) {
-      __builtin_nontemporal_store(v4f{ninf, ninf, ninf, ninf}, reinterpret_cast<v4f *>(row + c));
-    } else {
-      for (int i = 0; i < 4 && c + i < to; ++i) __builtin_nontemporal_store(ninf, row + c + i);
-    }
-  }
-}
-
-// One step of a reduce-scatter over the 16 lanes of a DPP row: x[0..2*HALF) holds
-// partial sums, the DPP control pairs each lane with one that differs in the bit
-// `upper` tests; the lane keeps the half that bit selects plus the partner's copy of
-// it, in x[0..HALF).
-template <int CTRL, int HALF>
-__device__ __forceinline__ void scatter_step(float (&x)[32], bool upper) {
-#pragma unroll
-  for (int j = 0; j < HALF; ++j) {
-    const float keep = upper ? x[j + HALF] : x[j];
-    const float send = upper ? x[j] : x[j + HALF];
-    x[j] = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), CTRL, 0xF, 0xF, false));
-  }
-}
-
 // e4m3 A operand (rows: qt parts) times e2m1 B operand (keys) with the keys' block scales
 __device__ __forceinline__ v4f mfma_qt_fp4(const v8i &a, const v8i &b, int scale_b) {
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
@@ -167,10 +141,10 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_fp4_kernel(PagedArgs a, 
         pq[8 * wd + 7] = fmaf(ws, b3[1], pq[8 * wd + 7]);
       }
     }
-    scatter_step<0x140, 16>(pq, n & 8);  // row_mirror: partner differs in bit 3
-    scatter_step<0x141, 8>(pq, n & 4);   // row_half_mirror: bits 0..2
-    scatter_step<0x1B, 4>(pq, n & 2);    // quad_perm [3,2,1,0]: bits 0, 1
-    scatter_step<0xB1, 2>(pq, n & 1);    // quad_perm [1,0,3,2]: bit 0
+    reduce_scatter_step<0x140, 16>(pq, n & 8);  // row_mirror: partner differs in bit 3
+    reduce_scatter_step<0x141, 8>(pq, n & 4);   // row_half_mirror: bits 0..2
+    reduce_scatter_step<0x1B, 4>(pq, n & 2);    // quad_perm [3,2,1,0]: bits 0, 1
+    reduce_scatter_step<0xB1, 2>(pq, n & 1);    // quad_perm [1,0,3,2]: bit 0
     const float q0 = pq[0], q1 = pq[1];
     float m = fmaxf(fabsf(q0), fabsf(q1));
 #pragma unroll
@@ -209,7 +183,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_fp4_kernel(PagedArgs a, 
   const int c_end = hi > s0 ? min(((hi + kChunk - 1) / kChunk) * kChunk, s1) : s0;
 #pragma unroll
   for (int rr = 0; rr < kRowsPerWave; ++rr)
-    if (active[rr]) fill_ninf(a.logits + int64_t(r_base + rr) * a.logits_row_stride, c_end, s1, lane);
+    if (active[rr]) fill_neg_inf(a.logits + int64_t(r_base + rr) * a.logits_row_stride, c_end, s1, lane);
 
   // wave w fetches run w of a chunk: the page of keys [c + 16 w, c + 16 w + 16) (inside
   // one page, since 16 divides the page size), then the run's values and scales; runs

@@ -35,32 +35,6 @@ constexpr int kMaxCache = 32768;  // keys kept in LDS (128 KiB)
 constexpr int kBins = 2048;       // digits 1 and 2: 11 bits; digit 3: 10 bits
 constexpr int kUnroll = 16;       // loads in flight per thread in the first pass
 
-__device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;  // -0.0 ranks with +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ int lane_prefix(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
-}
-
-// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS traffic): shifts of
-// 1, 2, 4 and 8 lanes inside each 16-lane row, then the last lane of rows 0 and 2
-// broadcast into rows 1 and 3, and lane 31 into rows 2 and 3. Lanes a move does not
-// reach add 0.
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
-  return x;
-}
-
-__device__ __forceinline__ int wave_sum(int x) { return __builtin_amdgcn_readlane(wave_incl_scan(x), 63); }
-
 // Candidate list size: long rows (few rows, 1024 threads) get more room, up to what
 // LDS holds beside a full key cache (160 KiB per workgroup).
 template <int NT>
@@ -76,43 +50,14 @@ struct __attribute__((aligned(16))) Smem {
   uint32_t cand[Cfg<NT>::kCand];  // (wave << 21) | low 21 bits of a key of the selected bin
   int wgt[Cfg<NT>::kWaves];       // per wave segment: keys above T
   int weq[Cfg<NT>::kWaves];       // per wave segment: keys equal to T
-  int sel_digit, sel_above, ncand;
+  int sel[2];  // selected digit, keys above it
+  int ncand;
 };
 
-// Wave 0 finds the digit d with (# keys above d) < kr <= (# at or above d) in
-// hist[0..NBINS) (larger digit = larger key) and publishes d and the count above
-// it; the barrier makes them visible to the workgroup. Two parallel steps, no serial
-// walk: each lane sums its NBINS/64 bins and a lane scan with a ballot names the lane
-// whose bins hold the kr-th key; then NBINS/64 lanes take one of that lane's bins
-// each (highest first), and a second scan and ballot name the bin.
+// select_bin over hist[0..NBINS), published to the workgroup in sm.sel
 template <int NT, int NBINS>
-__device__ void select_digit(Smem<NT> &sm, const uint32_t *hist, int kr) {
-  static_assert(NBINS % 256 == 0, "whole 16-byte loads per lane");
-  constexpr int kPer = NBINS / 64;
-  if ((threadIdx.x >> 6) == 0) {
-    const int lane = threadIdx.x & 63;
-    const int first = NBINS - (lane + 1) * kPer;  // this lane: bins [first, first + kPer), lane 0 highest
-    int local = 0;
-#pragma unroll
-    for (int q = 0; q < kPer / 4; ++q) {
-      const v4i x = *reinterpret_cast<const v4i *>(hist + first + 4 * q);
-      local += (x[0] + x[1]) + (x[2] + x[3]);
-    }
-    const int incl = wave_incl_scan(local);
-    const int run = incl - local;
-    const uint64_t hit = __ballot(run < kr && incl >= kr);
-    const int t = hit ? __builtin_ctzll(hit) : 0;  // one lane when 1 <= kr <= total
-    const int run_t = __builtin_amdgcn_readlane(run, t);
-    const int first_t = NBINS - (t + 1) * kPer;
-    const int v = lane < kPer ? int(hist[first_t + kPer - 1 - lane]) : 0;
-    const int iv = wave_incl_scan(v);
-    const uint64_t hit2 = __ballot(lane < kPer && run_t + iv >= kr);
-    const int j = hit2 ? __builtin_ctzll(hit2) : 0;
-    if (lane == j) {
-      sm.sel_digit = first_t + kPer - 1 - j;
-      sm.sel_above = run_t + iv - v;
-    }
-  }
+__device__ __forceinline__ void select_digit(Smem<NT> &sm, const uint32_t *hist, int kr) {
+  select_bin<NBINS>(hist, kr, sm.sel);
   __syncthreads();
 }
 
@@ -147,8 +92,8 @@ __device__ void finish_row(Smem<NT> &sm, KeyAt key_at, int n, int k, int32_t *ou
   int lo, hi;
   segment<NT, KPL>(n, wave, lo, hi);
 
-  const uint32_t d1 = uint32_t(sm.sel_digit);
-  int kr = k - sm.sel_above;  // keys still needed from bin d1
+  const uint32_t d1 = uint32_t(sm.sel[0]);
+  int kr = k - sm.sel[1];  // keys still needed from bin d1
   const int c1 = int(sm.hist[d1]);
   const bool whole_bin = c1 == kr;
   const bool use_cand = !whole_bin && c1 <= cand_cap;
@@ -206,8 +151,8 @@ __device__ void finish_row(Smem<NT> &sm, KeyAt key_at, int n, int k, int32_t *ou
     kr = 0;
   } else {
     select_digit<NT, kBins>(sm, sm.hist2, kr);
-    const uint32_t p2 = (d1 << 11) | uint32_t(sm.sel_digit);  // top 22 bits of T
-    kr -= sm.sel_above;
+    const uint32_t p2 = (d1 << 11) | uint32_t(sm.sel[0]);  // top 22 bits of T
+    kr -= sm.sel[1];
     if (use_cand) {
       const int nc = sm.ncand;
       for (int i = tid; i < nc; i += NT) {
@@ -229,8 +174,8 @@ __device__ void finish_row(Smem<NT> &sm, KeyAt key_at, int n, int k, int32_t *ou
     }
     __syncthreads();
     select_digit<NT, 1024>(sm, sm.hist, kr);
-    T = (p2 << 10) | uint32_t(sm.sel_digit);
-    kr -= sm.sel_above;  // ties (keys equal to T) still to take, >= 1
+    T = (p2 << 10) | uint32_t(sm.sel[0]);
+    kr -= sm.sel[1];  // ties (keys equal to T) still to take, >= 1
     if (use_cand) {
       const int nc = sm.ncand;
       for (int i = tid; i < nc; i += NT) {
@@ -314,9 +259,9 @@ __device__ void finish_cached(Smem<NT> &sm, const uint32_t *keys, int n, int k, 
   const int seg = (n + Cfg<NT>::kWaves * kStep - 1) / (Cfg<NT>::kWaves * kStep) * kStep;
   const int lo = min(n, wave * seg), hi = min(n, lo + seg);
 
-  const uint32_t d1 = uint32_t(sm.sel_digit);
+  const uint32_t d1 = uint32_t(sm.sel[0]);
   const uint32_t top = (d1 << 21) | 0x1FFFFFu;  // largest key of bin d1
-  int kr = k - sm.sel_above;
+  int kr = k - sm.sel[1];
   const bool whole_bin = int(sm.hist[d1]) == kr;
   __syncthreads();  // every thread has read hist before it is cleared below
 
@@ -369,8 +314,8 @@ __device__ void finish_cached(Smem<NT> &sm, const uint32_t *keys, int n, int k, 
     kr = 0;
   } else {
     select_digit<NT, kBins>(sm, sm.hist2, kr);
-    const uint32_t p2 = (d1 << 11) | uint32_t(sm.sel_digit);
-    kr -= sm.sel_above;
+    const uint32_t p2 = (d1 << 11) | uint32_t(sm.sel[0]);
+    kr -= sm.sel[1];
     const int nc = min(sm.ncand, Cfg<NT>::kCand);
     for (int i = tid; i < nc; i += NT) {
       const uint32_t key = (d1 << 21) | (sm.cand[i] & 0x1FFFFFu);
@@ -378,8 +323,8 @@ __device__ void finish_cached(Smem<NT> &sm, const uint32_t *keys, int n, int k, 
     }
     __syncthreads();
     select_digit<NT, 1024>(sm, sm.hist, kr);
-    T = (p2 << 10) | uint32_t(sm.sel_digit);
-    kr -= sm.sel_above;  // ties (keys equal to T) still to take, >= 1
+    T = (p2 << 10) | uint32_t(sm.sel[0]);
+    kr -= sm.sel[1];  // ties (keys equal to T) still to take, >= 1
     for (int i = tid; i < nc; i += NT) {
       const uint32_t c = sm.cand[i];
       const uint32_t key = (d1 << 21) | (c & 0x1FFFFFu);
@@ -450,8 +395,8 @@ __device__ void finish_half(Smem<NT> &sm, uint16_t *top16, const float *lr, int 
   const int seg = (n + Cfg<NT>::kWaves * kStep - 1) / (Cfg<NT>::kWaves * kStep) * kStep;
   const int lo = min(n, wave * seg), hi = min(n, lo + seg);
 
-  const uint32_t d1 = uint32_t(sm.sel_digit);
-  int kr = k - sm.sel_above;
+  const uint32_t d1 = uint32_t(sm.sel[0]);
+  int kr = k - sm.sel[1];
   const bool whole_bin = int(sm.hist[d1]) == kr;
   __syncthreads();  // every thread has read hist before it is cleared below
 
@@ -509,8 +454,8 @@ __device__ void finish_half(Smem<NT> &sm, uint16_t *top16, const float *lr, int 
     }
     __syncthreads();
     select_digit<NT, kBins>(sm, sm.hist2, kr);
-    const uint32_t p2 = (d1 << 11) | uint32_t(sm.sel_digit);
-    kr -= sm.sel_above;
+    const uint32_t p2 = (d1 << 11) | uint32_t(sm.sel[0]);
+    kr -= sm.sel[1];
     for (int i = tid; i < nc; i += NT) {
       const uint32_t c = sm.cand[i];
       const uint32_t key = (uint32_t(top16[c >> 16]) << 16) | (c & 0xFFFFu);
@@ -518,8 +463,8 @@ __device__ void finish_half(Smem<NT> &sm, uint16_t *top16, const float *lr, int 
     }
     __syncthreads();
     select_digit<NT, 1024>(sm, sm.hist, kr);
-    T = (p2 << 10) | uint32_t(sm.sel_digit);
-    kr -= sm.sel_above;  // ties (keys equal to T) still to take, >= 1
+    T = (p2 << 10) | uint32_t(sm.sel[0]);
+    kr -= sm.sel[1];  // ties (keys equal to T) still to take, >= 1
     const uint32_t tp = T >> 16;
     for (int i = tid; i < nc; i += NT) {
       const uint32_t c = sm.cand[i];
@@ -692,12 +637,12 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
   __syncthreads();
   select_digit<NT, kBins>(sm, sm.hist, k);
 
-  const int c1 = int(sm.hist[sm.sel_digit]);
-  if (cached && (c1 == k - sm.sel_above || c1 <= Cfg<NT>::kCand))
+  const int c1 = int(sm.hist[sm.sel[0]]);
+  if (cached && (c1 == k - sm.sel[1] || c1 <= Cfg<NT>::kCand))
     finish_cached<NT>(sm, s_keys, n, k, out);
   else if (cached)
     finish_row<NT, 8>(sm, [&](int i) { return s_keys[i]; }, n, k, out, sm.cand, Cfg<NT>::kCand);
-  else if (half && (c1 == k - sm.sel_above || c1 <= Cfg<NT>::kCand))
+  else if (half && (c1 == k - sm.sel[1] || c1 <= Cfg<NT>::kCand))
     finish_half<NT>(sm, s_top16, lr, n, k, out);
   else
     finish_row<NT, 16>(sm, [&](int i) { return order_key(lr[i]); }, n, k, out, s_keys, cache_cap);
@@ -705,7 +650,20 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
 
 }  // namespace
 
-hipError_t launch_topk(const TopkArgs &a, int, hipStream_t stream) {
+hipError_t launch_topk(const TopkArgs &a, int num_cus, void *scratch, size_t scratch_bytes, hipStream_t stream) {
+  // Few, long rows: several workgroups share each row (topk_coop.hip) when the
+  // caller's scratch holds the rows' records and the rows are 16-byte aligned. Up to
+  // 65536 keys a row fits one workgroup's LDS (whole keys or their top 16 bits) and the
+  // single-workgroup kernel is as fast or faster: the units of a shared row meet
+  // through device memory, about a microsecond a round trip (measured on an MI355X:
+  // 64 rows x 65536, 35 us shared against 28 us; 16 rows x 131072, 22 us against 76 us;
+  // one row of 2^20 keys, 41 us against 591 us).
+  if (scratch && a.width > kMaxCache * 2 && a.rows <= kCoopMaxRows && scratch_bytes >= topk_scratch_bytes(a.rows) &&
+      (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0 && a.logits_row_stride % 4 == 0 &&
+      int64_t(a.rows) * (int64_t(a.width) + 4) < (int64_t(1) << 30)) {
+    const int grid = topk_coop_grid(num_cus, a.rows, a.width);
+    if (grid > a.rows) return launch_topk_coop(a, scratch, grid, stream);
+  }
   // Many rows (narrow workgroups): a key cache of half the width, so rows longer than
   // it keep 16-bit key prefixes instead (finish_half) and four workgroups fit a CU's
   // LDS instead of three (8192 rows of 8192 keys: top-k 98 -> 86 us).

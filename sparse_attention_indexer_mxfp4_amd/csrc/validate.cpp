@@ -84,11 +84,10 @@ idx_status check_paged_mqa_logits(const idx_paged_cache *cache, const void *q, c
   return IDX_OK;
 }
 
-size_t topk_workspace_bytes(int32_t, int32_t, int32_t) { return 0; }
+size_t topk_workspace_bytes(int32_t rows, int32_t, int32_t) { return topk_scratch_bytes(rows); }
 
-idx_status check_topk(const void *logits, int64_t logits_row_stride, int32_t rows, int32_t width,
-                      const void *row_end, int32_t k, const void *out, int64_t out_row_stride,
-                      const void *workspace, size_t workspace_bytes, bool *empty) {
+idx_status check_topk_args(const void *logits, int64_t logits_row_stride, int32_t rows, int32_t width,
+                           const void *row_end, int32_t k, const void *out, int64_t out_row_stride, bool *empty) {
   *empty = false;
   if (rows < 0 || width < 0 || k < 1 || k > kMaxTopK) return IDX_ERR_SHAPE;
   if (rows == 0) {
@@ -99,6 +98,14 @@ idx_status check_topk(const void *logits, int64_t logits_row_stride, int32_t row
   if (width > 0 && !logits) return IDX_ERR_NULL;
   if (width > 0 && (logits_row_stride < width || !aligned(logits, 4))) return IDX_ERR_STRIDE;
   if (out_row_stride < k || !aligned(out, 4) || !aligned(row_end, 4)) return IDX_ERR_STRIDE;
+  return IDX_OK;
+}
+
+idx_status check_topk(const void *logits, int64_t logits_row_stride, int32_t rows, int32_t width,
+                      const void *row_end, int32_t k, const void *out, int64_t out_row_stride,
+                      const void *workspace, size_t workspace_bytes, bool *empty) {
+  const idx_status s = check_topk_args(logits, logits_row_stride, rows, width, row_end, k, out, out_row_stride, empty);
+  if (s != IDX_OK || *empty) return s;
   const size_t need = topk_workspace_bytes(rows, width, k);
   if (workspace_bytes < need) return IDX_ERR_WORKSPACE;
   if (need > 0 && !workspace) return IDX_ERR_NULL;

@@ -16,6 +16,17 @@ constexpr int32_t kMaxNextN = 4;
 constexpr int32_t kMaxBatch = 8192;
 constexpr int32_t kMaxTopK = 65536;
 
+// The several-workgroups-per-row top-k: up to kCoopMaxRows rows, at most kCoopMaxUnits
+// workgroups. Its scratch holds one 16-byte record per workgroup, then one
+// kCoopRowBytes record per row.
+constexpr int kCoopMaxRows = 256;
+constexpr int kCoopMaxUnits = 2048;
+constexpr size_t kCoopUnitBytes = 16;
+constexpr size_t kCoopRowBytes = 36928;
+constexpr size_t topk_scratch_bytes(int rows) {
+  return rows < 1 || rows > kCoopMaxRows ? 0 : size_t(kCoopMaxUnits) * kCoopUnitBytes + size_t(rows) * kCoopRowBytes;
+}
+
 size_t page_bytes(int32_t fmt, int32_t page_size, int32_t head_dim);
 
 idx_status check_cache(const idx_paged_cache *cache);
@@ -34,6 +45,10 @@ idx_status check_paged_mqa_logits(const idx_paged_cache *cache, const void *q, c
                                   size_t workspace_bytes, bool *empty);
 
 size_t topk_workspace_bytes(int32_t rows, int32_t width, int32_t k);
+
+// idx_topk's checks of everything but the workspace
+idx_status check_topk_args(const void *logits, int64_t logits_row_stride, int32_t rows, int32_t width,
+                           const void *row_end, int32_t k, const void *out, int64_t out_row_stride, bool *empty);
 
 idx_status check_topk(const void *logits, int64_t logits_row_stride, int32_t rows, int32_t width,
                       const void *row_end, int32_t k, const void *out, int64_t out_row_stride,

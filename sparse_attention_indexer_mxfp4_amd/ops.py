@@ -40,6 +40,25 @@ def _contig(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+_WORKSPACES: dict = {}
+
+
+def topk_workspace(nbytes: int, device) -> torch.Tensor | None:
+    """A zero-filled scratch buffer of at least nbytes for the top-k calls, kept per
+    device and reused: the calls leave it zero-filled, as they need it at their start.
+    Calls that share it must not overlap (one stream, or ordered streams); a caller that
+    runs top-k on several streams at once passes a workspace of its own to each."""
+    if nbytes == 0:
+        return None
+    dev = torch.device(device)
+    key = (dev.type, dev.index)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def page_bytes(fmt: int, page_size: int, head_dim: int = HEAD_DIM) -> int:
     return int(_abi.lib().idx_page_bytes(fmt, page_size, head_dim))
 
@@ -169,7 +188,7 @@ def idx_candidate_blocks(block_max: torch.Tensor, row_end: torch.Tensor, block_s
         out = torch.empty((rows, n_cand), dtype=torch.int32, device=block_max.device)
     lib = _abi.lib()
     need = lib.idx_topk_workspace(rows, nb, n_cand)
-    workspace = torch.empty(need, dtype=torch.uint8, device=block_max.device) if need else None
+    workspace = topk_workspace(need, block_max.device)
     _abi.check(lib.idx_candidate_blocks(_ptr(block_max), block_max.stride(0), rows, nb, _ptr(row_end), block_size,
                                         n_cand, _ptr(out), out.stride(0), _ptr(workspace), need, _stream()))
     return out
@@ -227,7 +246,9 @@ def idx_remap_compact_topk(topk: torch.Tensor, cand: torch.Tensor, block_size: i
 def idx_topk(logits: torch.Tensor, row_start: torch.Tensor | None, row_end: torch.Tensor, k: int,
              out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Per-row top-k over [row_start, row_end) -> [rows, k] int32 (column - start, ascending
-    column order, -1 padded)."""
+    column order, -1 padded). ``workspace``: uint8 device memory of at least
+    idx_topk_workspace() bytes, zero-filled before its first use (the call leaves it
+    so); by default the per-device buffer of ``topk_workspace``."""
     _need(logits, torch.float32, "logits"); _need(row_end, torch.int32, "row_end")
     _contig(row_end, "row_end")
     if row_start is not None:
@@ -239,8 +260,8 @@ def idx_topk(logits: torch.Tensor, row_start: torch.Tensor | None, row_end: torc
         out = torch.empty((rows, k), dtype=torch.int32, device=logits.device)
     lib = _abi.lib()
     need = lib.idx_topk_workspace(rows, width, k)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    if workspace is None:
+        workspace = topk_workspace(need, logits.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _abi.check(lib.idx_topk(_ptr(logits), logits.stride(0), rows, width, _ptr(row_start), _ptr(row_end), k,
                             _ptr(out), out.stride(0), _ptr(workspace), ws_bytes, _stream()))

@@ -141,11 +141,19 @@ def test_paged_checks(lib):
 def test_workspace_queries(lib):
     c = _cache()
     assert lib.idx_paged_mqa_logits_workspace(4, 1, 64, ctypes.byref(c)) == 0
-    assert lib.idx_topk_workspace(4, 1000, 16) == 0
+    # top-k: 4096 workgroup records of 16 bytes and one 28736-byte record per row, for
+    # 1..256 rows (several workgroups per row); none beyond
+    assert lib.idx_topk_workspace(4, 1000, 16) == 2048 * 16 + 4 * 36928
+    assert lib.idx_topk_workspace(256, 1000, 16) == 2048 * 16 + 256 * 36928
+    assert lib.idx_topk_workspace(257, 1000, 16) == 0
+    assert lib.idx_topk_workspace(0, 1000, 16) == 0
+
+
+WS4 = 2048 * 16 + 4 * 36928  # idx_topk_workspace for 4 rows
 
 
 def _topk(lib, **kw):
-    a = dict(L=P, ls=1000, rows=4, width=1000, rs=None, re=P, k=16, out=P, os=16, ws=None, wsb=0)
+    a = dict(L=P, ls=1000, rows=4, width=1000, rs=None, re=P, k=16, out=P, os=16, ws=P, wsb=WS4)
     a.update(kw)
     return lib.idx_topk(a["L"], a["ls"], a["rows"], a["width"], a["rs"], a["re"], a["k"], a["out"], a["os"], a["ws"],
                         a["wsb"], None)
@@ -162,6 +170,9 @@ def test_topk_checks(lib):
     assert _topk(lib, ls=999) == STRIDE
     assert _topk(lib, os=15) == STRIDE
     assert _topk(lib, out=P + 2) == STRIDE
+    assert _topk(lib, wsb=WS4 - 1) == WORKSPACE
+    assert _topk(lib, ws=None) == NULL
+    assert _topk(lib, rows=300, ws=None, wsb=0) != WORKSPACE  # many rows: no workspace needed
 
 
 def test_k_store_and_q_quant_checks(lib):

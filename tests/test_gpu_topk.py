@@ -62,6 +62,89 @@ def test_topk_many_rows():
     np.testing.assert_array_equal(got, indexer.topk(L.astype(np.float64), None, ends, k))
 
 
+# ---- several workgroups per row (up to 256 rows of more than 65536 columns, 16-byte aligned)
+def _oracle(L, starts, ends, k):
+    return indexer.topk(L.astype(np.float64), starts, ends, k)
+
+
+def test_topk_coop_repeated_calls():
+    # the per-row records in the workspace must come back zeroed after every call:
+    # three calls in a row on different data and row counts, each against the oracle
+    rng = np.random.default_rng(11)
+    for rows, width, k in ((32, 100000, 2048), (7, 70000, 700), (64, 131072, 512)):
+        L = rng.standard_normal((rows, width)).astype(np.float32)
+        ends = rng.integers(1, width + 1, rows)
+        ends[0] = width
+        ends[1] = k  # a row of exactly k keys: no selection
+        ends[2] = 70000  # one unit may hold it whole
+        starts = rng.integers(0, 7, rows)
+        np.testing.assert_array_equal(_run(L, starts, ends, k), _oracle(L, starts, ends, k))
+
+
+def test_topk_coop_full_rows_several_passes():
+    # 256 rows of 131072 keys: more units than the device holds at once would be needed
+    # for units that fit the registers, so every phase re-reads its columns in passes
+    rng = np.random.default_rng(12)
+    rows, width, k = 256, 131072, 2048
+    L = rng.standard_normal((rows, width)).astype(np.float32)
+    ends = np.full(rows, width)
+    ends[::5] = rng.integers(k + 1, width, ends[::5].size)
+    np.testing.assert_array_equal(_run(L, None, ends, k), _oracle(L, None, ends, k))
+
+
+@pytest.mark.parametrize("ties", [False, True])
+def test_topk_coop_one_long_row(ties):
+    # one row of a million keys spread over hundreds of workgroups
+    rng = np.random.default_rng(13)
+    width, k = 1_000_000, 2048
+    L = rng.standard_normal((1, width)).astype(np.float32)
+    if ties:
+        L = np.round(L * 4) / 4
+    ends = np.array([width - 3])
+    starts = np.array([5])
+    np.testing.assert_array_equal(_run(L, starts, ends, k), _oracle(L, starts, ends, k))
+
+
+@pytest.mark.parametrize("shared_prefix", [False, True])
+def test_topk_coop_crowded_bin(shared_prefix):
+    # The k-th key sits in a crowd of keys sharing its top 11 bits - more than the
+    # per-row list holds - so the units meet again over a second row histogram. With
+    # distinct 22-bit prefixes (values 1 + i 2^-13) the crowd's prefix of T is small and
+    # goes to the list; with one shared prefix (values 1 + j 2^-23, j < 1024) it
+    # overflows too, and T comes from a third histogram. 500 keys lie above the crowd;
+    # ties go to the lowest columns.
+    rng = np.random.default_rng(14 + shared_prefix)
+    rows, width, k = 3, 100000, 2048
+    L = rng.standard_normal((rows, width)).astype(np.float32) - 10.0
+    for r in range(rows):
+        cols = rng.choice(width, 6000, replace=False)
+        step, top = (2.0 ** -23, 1024) if shared_prefix else (2.0 ** -13, 2048)
+        L[r, cols] = (1.0 + rng.integers(0, top, 6000) * step).astype(np.float32)
+        L[r, rng.choice(np.setdiff1d(np.arange(width), cols), 500, replace=False)] = 5.0
+    ends = np.full(rows, width)
+    np.testing.assert_array_equal(_run(L, None, ends, k), _oracle(L, None, ends, k))
+
+
+@pytest.mark.parametrize("rows,width,k", [(32, 100000, 2048), (5, 300000, 64)])
+def test_topk_coop_matches_one_workgroup_per_row(rows, width, k):
+    # the same rows through both kernels: a row pointer off 16-byte alignment takes the
+    # one-workgroup-per-row kernel
+    rng = np.random.default_rng(rows + k)
+    L = rng.standard_normal((rows, width + 1)).astype(np.float32)
+    ends = rng.integers(0, width + 1, rows)
+    lt = torch.from_numpy(L).to(DEV)
+    en = torch.from_numpy(ends.astype(np.int32)).to(DEV)
+    aligned = torch.empty((rows, -(-width // 4) * 4), dtype=torch.float32, device=DEV)[:, :width]
+    aligned.copy_(lt[:, 1:])
+    off = lt[:, 1:]  # rows start 4 bytes past a 16-byte boundary
+    a = ops.idx_topk(aligned, None, en, k)
+    b = ops.idx_topk(off, None, en, k)
+    torch.cuda.synchronize()
+    want = _oracle(L[:, 1:], None, ends, k)
+    np.testing.assert_array_equal(a.cpu().numpy(), want)
+    np.testing.assert_array_equal(b.cpu().numpy(), want)
+
+
 @pytest.mark.parametrize("next_n,valid", [(1, False), (2, True)])
 def test_topk_to_slots_matches_oracle(next_n, valid):
     from oracle import indexer as oi
