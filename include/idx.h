@@ -199,6 +199,22 @@ idx_status idx_topk(const float *logits, int64_t logits_row_stride, int32_t rows
  * else 0. */
 size_t idx_topk_workspace(int32_t rows, int32_t width, int32_t k);
 
+/*
+ * idx_topk_noalloc - idx_topk for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments and output as idx_topk, without the workspace.
+ *   The several-workgroups-per-row path keeps its records in an array the library
+ *   owns instead: 2048 * 16 + 256 * 36928 bytes (about 9 MiB) of device memory per
+ *   GPU, enough for the 256 rows that path takes at most, held until the process
+ *   ends. The array is zero when the library loads and every call leaves it zero.
+ *   All calls on one GPU share it: calls that overlap on one GPU (several streams,
+ *   several host threads) race, and their outputs are unspecified.
+ *   The call allocates nothing and calls no allocating routine. Errors as idx_topk;
+ *   IDX_ERR_DEVICE also when the array's address cannot be looked up.
+ */
+idx_status idx_topk_noalloc(const float *logits, int64_t logits_row_stride, int32_t rows, int32_t width,
+                            const int32_t *row_start, const int32_t *row_end, int32_t k, int32_t *out,
+                            int64_t out_row_stride, hipStream_t stream);
 
 /*
  * idx_k_store - quantise key rows and write them into their cache slots.

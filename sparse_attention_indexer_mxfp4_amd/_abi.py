@@ -25,7 +25,7 @@ EXPORTS = (
     "idx_page_bytes", "idx_mqa_logits", "idx_paged_mqa_logits", "idx_paged_mqa_logits_workspace", "idx_topk",
     "idx_topk_workspace", "idx_k_store", "idx_q_quant", "idx_k_norm_rope_store", "idx_q_rope_quant",
     "idx_topk_to_slots", "idx_paged_mqa_logits_block_max", "idx_candidate_blocks", "idx_apply_candidate_mask",
-    "idx_paged_mqa_logits_gather", "idx_remap_compact_topk", "idx_paged_prefill_logits",
+    "idx_paged_mqa_logits_gather", "idx_remap_compact_topk", "idx_paged_prefill_logits", "idx_topk_noalloc",
     "idx_status_str", "idx_abi_version",
 )
 
@@ -68,6 +68,7 @@ def _declare(lib: ctypes.CDLL) -> None:
         "idx_paged_mqa_logits_workspace": (_SZ, [_I32, _I32, _I32, cache_p]),
         "idx_topk": (_I32, [_P, _I64, _I32, _I32, _P, _P, _I32, _P, _I64, _P, _SZ, _P]),
         "idx_topk_workspace": (_SZ, [_I32, _I32, _I32]),
+        "idx_topk_noalloc": (_I32, [_P, _I64, _I32, _I32, _P, _P, _I32, _P, _I64, _P]),
         "idx_k_store": (_I32, [cache_p, _P, _I32, _I64, _P, _I32, _P]),
         "idx_q_quant": (_I32, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _P, _P, _P]),
         "idx_k_norm_rope_store": (_I32, [cache_p, _P, _I32, _I64, _P, _P, _I32, _I32, _P, _F32, _P, _I32, _P]),

@@ -298,6 +298,24 @@ idx_status idx_topk(const float *logits, int64_t logits_row_stride, int32_t rows
   return launched(idx::launch_topk(a, cus, workspace, workspace_bytes, stream));
 }
 
+idx_status idx_topk_noalloc(const float *logits, int64_t logits_row_stride, int32_t rows, int32_t width,
+                            const int32_t *row_start, const int32_t *row_end, int32_t k, int32_t *out,
+                            int64_t out_row_stride, hipStream_t stream) {
+  bool empty = false;
+  idx_status s = idx::check_topk_args(logits, logits_row_stride, rows, width, row_end, k, out, out_row_stride,
+                                      &empty);
+  if (s != IDX_OK || empty) return s;
+  int cus = 0;
+  if ((s = current_device(&cus)) != IDX_OK) return s;
+  size_t bytes = 0;
+  void *ws = idx::topk_static_scratch(&bytes);
+  if (!ws) return IDX_ERR_DEVICE;
+  // more rows than the array has records for never take the path that uses it
+  if (idx::topk_scratch_bytes(rows) > bytes) return IDX_ERR_WORKSPACE;
+  idx::TopkArgs a{logits, logits_row_stride, rows, width, row_start, row_end, k, out, out_row_stride, 1};
+  return launched(idx::launch_topk(a, cus, ws, bytes, stream));
+}
+
 idx_status idx_k_store(const idx_paged_cache *cache, const void *k, int32_t k_dtype, int64_t k_row_stride,
                        const int64_t *slot_mapping, int32_t N, hipStream_t stream) {
   bool empty = false;

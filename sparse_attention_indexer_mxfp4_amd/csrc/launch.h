@@ -169,7 +169,9 @@ hipError_t launch_topk(const TopkArgs &a, int num_cus, void *scratch, size_t scr
 
 int topk_coop_grid(int num_cus, int rows, int width);  // its grid for these rows (0: cannot run)
 hipError_t launch_topk_coop(const TopkArgs &a, void *scratch, int grid, hipStream_t stream);
-
+// The current device's address of the library-owned top-k scratch (topk_scratch_bytes(
+// kCoopMaxRows) bytes, in *bytes), looked up once per device; nullptr on failure.
+void *topk_static_scratch(size_t *bytes);
 hipError_t launch_k_store(const KStoreArgs &a, hipStream_t stream);
 hipError_t launch_q_quant(const QQuantArgs &a, hipStream_t stream);
 hipError_t launch_q_rope_quant(const QRopeArgs &a, hipStream_t stream);

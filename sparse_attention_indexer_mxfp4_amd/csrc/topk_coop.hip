@@ -584,7 +584,30 @@ __global__ __launch_bounds__(kNT) void topk_coop_kernel(TopkArgs a, uint8_t *ws)
   }
 }
 
+// The records of the cooperative kernel for up to kCoopMaxRows rows, owned by the
+// library for callers that cannot allocate (idx_topk_noalloc). Zero when the code object
+// loads, and every call leaves it zero. Host code never passes this name to a kernel:
+// it is a host-side stand-in; the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[topk_scratch_bytes(kCoopMaxRows)];
+
 }  // namespace
+
+void *topk_static_scratch(size_t *bytes) {
+  constexpr int kDevices = 64;
+  static std::mutex mu;
+  static void *addr[kDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // this device is current: its own copy of the array
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    addr[dev] = p;
+  }
+  *bytes = sizeof(scratch);
+  return addr[dev];
+}
 
 // Workgroups of the cooperative kernel for these rows: enough units of at most kCap
 // columns for rows of `width`, no more than the device holds at once (0: it cannot
