@@ -169,6 +169,10 @@ hipError_t launch_topk(const TopkArgs &a, int num_cus, void *scratch, size_t scr
 
 int topk_coop_grid(int num_cus, int rows, int width);  // its grid for these rows (0: cannot run)
 hipError_t launch_topk_coop(const TopkArgs &a, void *scratch, int grid, hipStream_t stream);
+// One 256-thread workgroup per row with the row's keys in registers (no scratch), for
+// rows of at most topk_solo_cap() columns (the width bounds them).
+int topk_solo_cap();
+hipError_t launch_topk_solo(const TopkArgs &a, hipStream_t stream);
 // The current device's address of the library-owned top-k scratch (topk_scratch_bytes(
 // kCoopMaxRows) bytes, in *bytes), looked up once per device; nullptr on failure.
 void *topk_static_scratch(size_t *bytes);

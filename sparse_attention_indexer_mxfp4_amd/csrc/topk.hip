@@ -658,12 +658,20 @@ hipError_t launch_topk(const TopkArgs &a, int num_cus, void *scratch, size_t scr
   // through device memory, about a microsecond a round trip (measured on an MI355X:
   // 64 rows x 65536, 35 us shared against 28 us; 16 rows x 131072, 22 us against 76 us;
   // one row of 2^20 keys, 41 us against 591 us).
+  const bool rows16 = (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0 && a.logits_row_stride % 4 == 0;
   if (scratch && a.width > kMaxCache * 2 && a.rows <= kCoopMaxRows && scratch_bytes >= topk_scratch_bytes(a.rows) &&
-      (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0 && a.logits_row_stride % 4 == 0 &&
-      int64_t(a.rows) * (int64_t(a.width) + 4) < (int64_t(1) << 30)) {
+      rows16 && int64_t(a.rows) * (int64_t(a.width) + 4) < (int64_t(1) << 30)) {
     const int grid = topk_coop_grid(num_cus, a.rows, a.width);
     if (grid > a.rows) return launch_topk_coop(a, scratch, grid, stream);
   }
+  // Many rows of at most 8192 columns: one 256-thread workgroup per row with the row's
+  // keys in registers through the selection (topk_coop.hip), no key cache in LDS, so
+  // five workgroups fit a compute unit instead of four (8192 rows of the causal
+  // 8192-key chunk: 89 -> 63 us on an MI355X). With fewer rows the 1024-thread
+  // workgroups below finish each row sooner (a 64-row candidate pool: 6.2 against
+  // 8.6 us), and a 1024-thread register version for rows up to 32768 was slower than
+  // the LDS cache on a 32-row decode step (15.0 against 11.7 us).
+  if (rows16 && a.rows >= 1024 && a.width <= topk_solo_cap()) return launch_topk_solo(a, stream);
   // Many rows (narrow workgroups): a key cache of half the width, so rows longer than
   // it keep 16-bit key prefixes instead (finish_half) and four workgroups fit a CU's
   // LDS instead of three (8192 rows of 8192 keys: top-k 98 -> 86 us).

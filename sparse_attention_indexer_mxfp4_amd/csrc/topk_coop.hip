@@ -56,12 +56,8 @@
 namespace idx {
 namespace {
 
-constexpr int kNT = 256;
-constexpr int kWaves = kNT / 64;
-constexpr int kKPL = 16;                    // keys per lane held in registers
-constexpr int kSteps = kKPL / 4;            // 256-key steps of a wave (4 consecutive keys per lane)
-constexpr int kWaveCap = 64 * kKPL;         // keys a wave holds per pass
-constexpr int kCap = kWaves * kWaveCap;     // keys a unit holds per pass
+constexpr int kNT = 256;                    // threads of a shared-row unit
+constexpr int kKPL = 16;                    // keys per lane a shared-row unit holds in registers
 constexpr int kMinSeg = 1024;               // smallest unit of a multi-unit row, in columns
 constexpr int kBins = 2048;
 constexpr int kList = 4096;                 // list entries per row
@@ -126,14 +122,15 @@ __device__ __forceinline__ void wait_for(const uint32_t *ctr, uint32_t target) {
   __syncthreads();
 }
 
-// sum of one value per thread over the workgroup (every thread gets it)
+// sum of one value per thread over a workgroup of NT threads (every thread gets it)
+template <int NT>
 __device__ __forceinline__ int block_sum(int v, int *scratch) {
   const int s = wave_sum(v);
   if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = s;
   __syncthreads();
   int t = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) t += scratch[w];
+  for (int w = 0; w < NT / 64; ++w) t += scratch[w];
   __syncthreads();
   return t;
 }
@@ -148,71 +145,92 @@ __device__ __forceinline__ int find_unit_row(const int *pref, int n, int g) {
   return lo;
 }
 
+template <int NT>
 __device__ __forceinline__ void zero_lds(uint32_t *p, int n) {
-  for (int i = threadIdx.x; i < n; i += kNT) p[i] = 0u;
+  for (int i = threadIdx.x; i < n; i += NT) p[i] = 0u;
 }
 
-__global__ __launch_bounds__(kNT) void topk_coop_kernel(TopkArgs a, uint8_t *ws) {
-  __shared__ int s_pref[kCoopMaxRows + 1];
-  __shared__ int s_st[kCoopMaxRows], s_en[kCoopMaxRows];
-  // [0, kList): the row's list (or a copy of a row histogram); [kList, kList + kBins):
-  // this unit's histograms
-  __shared__ __attribute__((aligned(16))) uint32_t s_big[kList + kBins];
+// NT threads, KPL keys per lane in registers. SOLO: workgroup r selects row r alone,
+// the caller guarantees width <= NT * KPL (every row fits the registers at once) and no
+// scratch is used; otherwise the shared-row kernel described above.
+template <int NT, int KPL, bool SOLO>
+__global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a, uint8_t *ws) {
+  constexpr int kWaves = NT / 64;
+  constexpr int kSteps = KPL / 4;          // 256-key steps of a wave (4 consecutive keys per lane)
+  constexpr int kWaveCap = 64 * KPL;       // keys a wave holds per pass
+  __shared__ int s_pref[SOLO ? 1 : kCoopMaxRows + 1];
+  __shared__ int s_st[SOLO ? 1 : kCoopMaxRows], s_en[SOLO ? 1 : kCoopMaxRows];
+  // [0, kList): the row's list (or a copy of a row histogram); then this unit's
+  // histograms (a solo row needs only those)
+  __shared__ __attribute__((aligned(16))) uint32_t s_big[(SOLO ? 0 : kList) + kBins];
   __shared__ int s_red[kWaves];
   __shared__ int s_sel[2];
   __shared__ int s_wcnt[2][kWaves];
   __shared__ int s_slot[kWaves];
   __shared__ int s_last;
   uint32_t *const s_list = s_big;
-  uint32_t *const s_h = s_big + kList;
+  uint32_t *const s_h = s_big + (SOLO ? 0 : kList);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rows = a.rows, k = a.k;
   UnitInfo *const info = reinterpret_cast<UnitInfo *>(ws);
   RowState *const state = reinterpret_cast<RowState *>(ws + size_t(kCoopMaxUnits) * sizeof(UnitInfo));
 
-  // ---- the unit table (identical in every workgroup) ---------------------------------
-  int units = 0, span = 0;
-  if (tid < rows) {
-    const int st0 = a.row_start ? min(max(a.row_start[tid], 0), a.width) : 0;
-    const int e_in = max(a.row_end[tid], 0);
+  auto clamp_row = [&](int row, int &st0, int &en) {
+    st0 = a.row_start ? min(max(a.row_start[row], 0), a.width) : 0;
+    const int e_in = max(a.row_end[row], 0);
     const int en0 = min(a.end_div == 1 ? e_in : e_in / a.end_div + (e_in % a.end_div != 0), a.width);
-    const int en = max(en0, st0);
-    s_st[tid] = st0;
-    s_en[tid] = en;
-    if (en - st0 > k) span = en - (st0 & ~3);  // columns from the aligned start
+    en = max(en0, st0);
+  };
+  int r, g0 = 0, u = 0, nu = 1, seg = 0, st0, en;
+  if constexpr (SOLO) {
+    r = blockIdx.x;
+    clamp_row(r, st0, en);
+    seg = en - (st0 & ~3);
+  } else {
+    // ---- the unit table (identical in every workgroup) -------------------------------
+    int units = 0, span = 0;
+    if (tid < rows) {
+      int s0, e0;
+      clamp_row(tid, s0, e0);
+      s_st[tid] = s0;
+      s_en[tid] = e0;
+      if (e0 - s0 > k) span = e0 - (s0 & ~3);  // columns from the aligned start
+    }
+    const int total_span = block_sum<NT>(span, s_red);
+    const int free_units = max(1, int(gridDim.x) - rows);
+    seg = max(kMinSeg, ((total_span + free_units - 1) / free_units + 255) & ~255);
+    if (tid < rows) units = span > 0 ? (span + seg - 1) / seg : 1;
+    int n_units = 0;
+    const int first = block_excl_scan<NT>(units, s_red, &n_units);
+    if (tid < rows) s_pref[tid] = first;
+    if (tid == 0) s_pref[rows] = n_units;
+    __syncthreads();
+    const int g = blockIdx.x;
+    if (g >= n_units) return;
+    r = find_unit_row(s_pref, rows, g);
+    g0 = s_pref[r];
+    u = g - g0;
+    nu = s_pref[r + 1] - g0;
+    st0 = s_st[r];
+    en = s_en[r];
   }
-  const int total_span = block_sum(span, s_red);
-  const int free_units = max(1, int(gridDim.x) - rows);
-  const int seg = max(kMinSeg, ((total_span + free_units - 1) / free_units + 255) & ~255);
-  if (tid < rows) units = span > 0 ? (span + seg - 1) / seg : 1;
-  int n_units = 0;
-  const int first = block_excl_scan<kNT>(units, s_red, &n_units);
-  if (tid < rows) s_pref[tid] = first;
-  if (tid == 0) s_pref[rows] = n_units;
-  __syncthreads();
-
-  const int g = blockIdx.x;
-  if (g >= n_units) return;
-  const int r = find_unit_row(s_pref, rows, g);
-  const int g0 = s_pref[r];
-  const int u = g - g0, nu = s_pref[r + 1] - g0;
-  const int st0 = s_st[r], en = s_en[r], n = en - st0;
+  const int n = en - st0;
   int32_t *out = a.out + int64_t(r) * a.out_row_stride;
   if (n <= k) {
-    for (int i = tid; i < k; i += kNT) out[i] = i < n ? i : -1;
+    for (int i = tid; i < k; i += NT) out[i] = i < n ? i : -1;
     return;
   }
-  const bool solo = nu == 1;
-  RowState &rs = state[r];
-  UnitInfo *const ui = info + g;
+  const bool solo = SOLO || nu == 1;
+  RowState &rs = state[SOLO ? 0 : r];
+  UnitInfo *const ui = info + (SOLO ? 0 : g0 + u);
 
-  // ---- this unit's columns, four wave segments of whole 256-key steps -----------------
+  // ---- this unit's columns, wave segments of whole 256-key steps ----------------------
   const int a0 = st0 & ~3;
   const int lo = a0 + u * seg, hi = min(en, lo + seg);
   const int wseg = ((hi - lo + kWaves - 1) / kWaves + 255) & ~255;
   const int wlo = min(hi, lo + wave * wseg), whi = min(hi, wlo + wseg);
-  const bool single = wseg <= kWaveCap;  // the segment fits the registers: one load
+  const bool single = SOLO || wseg <= kWaveCap;  // the segment fits the registers: one load
   const float *lr = a.logits + int64_t(r) * a.logits_row_stride;
   const buffer_rsrc rsrc = make_rsrc(lr, uint32_t(en) * 4u);
 
@@ -249,19 +267,19 @@ __global__ __launch_bounds__(kNT) void topk_coop_kernel(TopkArgs a, uint8_t *ws)
     }
   };
   auto flush = [&](uint32_t *dst, int nbins) {
-    for (int b = tid; b < nbins; b += kNT) {
+    for (int b = tid; b < nbins; b += NT) {
       const uint32_t c = s_h[b];
       if (c) add(dst + b, c);
     }
   };
   // a row histogram of nbins words into s_list (copy)
   auto read_hist = [&](const uint32_t *src, int nbins) {
-    for (int i = 4 * tid; i < nbins; i += 4 * kNT)
+    for (int i = 4 * tid; i < nbins; i += 4 * NT)
       *reinterpret_cast<v4i *>(s_list + i) = ld16(src, uint32_t(nbins) * 4u, uint32_t(i) * 4u);
   };
   // local histogram of the keys `pick` accepts, bin(key) in [0, nbins)
   auto local_hist = [&](int nbins, auto &&pick, auto &&bin) {
-    zero_lds(s_h, nbins);
+    zero_lds<NT>(s_h, nbins);
     __syncthreads();
     walk([&](const uint32_t (&key)[4], int) {
 #pragma unroll
@@ -309,18 +327,18 @@ __global__ __launch_bounds__(kNT) void topk_coop_kernel(TopkArgs a, uint8_t *ws)
   };
   // the row's list of c entries into s_list
   auto read_list = [&](int c) {
-    for (int i = 4 * tid; i < c; i += 4 * kNT)
+    for (int i = 4 * tid; i < c; i += 4 * NT)
       *reinterpret_cast<v4i *>(s_list + i) = ld16(rs.list, uint32_t(c) * 4u, uint32_t(i) * 4u);
   };
   // sum of field f of the records of the row's units before this one
   auto units_before = [&](int f) {
     int x = 0;
-    for (int v = tid; v < u; v += kNT) x += ld16(info + g0 + v, 16u, 0u)[f];
-    return block_sum(x, s_red);
+    for (int v = tid; v < u; v += NT) x += ld16(info + g0 + v, 16u, 0u)[f];
+    return block_sum<NT>(x, s_red);
   };
 
   // ---- 1. digit-1 histogram ----------------------------------------------------------
-  zero_lds(s_h, kBins);
+  zero_lds<NT>(s_h, kBins);
   __syncthreads();
   walk([&](const uint32_t (&key)[4], int) {
 #pragma unroll
@@ -359,7 +377,7 @@ __global__ __launch_bounds__(kNT) void topk_coop_kernel(TopkArgs a, uint8_t *ws)
         kr3 = kr2 - s_sel[1];
       }
     }
-  } else {
+  } else if constexpr (!SOLO) {
     // ---- 1 (cont). the row histogram; bin d1 -----------------------------------------
     flush(rs.h1, kBins);
     arrive(&rs.arrive[0]);
@@ -372,8 +390,8 @@ __global__ __launch_bounds__(kNT) void topk_coop_kernel(TopkArgs a, uint8_t *ws)
     const int c1 = int(s_list[d1]);
     const bool whole1 = c1 == kr1;
     int mine = 0;
-    for (int b = tid; b < kBins; b += kNT) mine += int(b > int(d1) || (whole1 && b == int(d1))) * int(s_h[b]);
-    const int above1 = block_sum(mine, s_red);
+    for (int b = tid; b < kBins; b += NT) mine += int(b > int(d1) || (whole1 && b == int(d1))) * int(s_h[b]);
+    const int above1 = block_sum<NT>(mine, s_red);
     if (tid == 0) st(reinterpret_cast<uint32_t *>(&ui->above1), uint32_t(above1));
     // mode 0: bin d1 whole; 1: its keys in the list; 2: overflow (more meetings)
     const int mode = whole1 ? 0 : (c1 <= kList ? 1 : 2);
@@ -394,9 +412,9 @@ __global__ __launch_bounds__(kNT) void topk_coop_kernel(TopkArgs a, uint8_t *ws)
     } else if (mode == 1) {
       // the row's keys of bin d1, finished here: digit 2, then digit 3, over the list
       read_list(c1);
-      zero_lds(s_h, kBins);
+      zero_lds<NT>(s_h, kBins);
       __syncthreads();
-      for (int i = tid; i < c1; i += kNT) atomicAdd(&s_h[(s_list[i] >> 10) & uint32_t(kBins - 1)], 1u);
+      for (int i = tid; i < c1; i += NT) atomicAdd(&s_h[(s_list[i] >> 10) & uint32_t(kBins - 1)], 1u);
       __syncthreads();
       select(s_h, kBins, kr1);
       const uint32_t d2 = uint32_t(s_sel[0]);
@@ -407,9 +425,9 @@ __global__ __launch_bounds__(kNT) void topk_coop_kernel(TopkArgs a, uint8_t *ws)
       if (whole2) {
         T = (p2 << 10) - 1u;
       } else {
-        zero_lds(s_h, 1024);
+        zero_lds<NT>(s_h, 1024);
         __syncthreads();
-        for (int i = tid; i < c1; i += kNT)
+        for (int i = tid; i < c1; i += NT)
           if (((s_list[i] >> 10) & uint32_t(kBins - 1)) == d2) atomicAdd(&s_h[s_list[i] & 1023u], 1u);
         __syncthreads();
         select(s_h, 1024, kr2);
@@ -420,14 +438,14 @@ __global__ __launch_bounds__(kNT) void topk_coop_kernel(TopkArgs a, uint8_t *ws)
       // 21 bits order them)
       const uint32_t tl = T & 0x1FFFFFu;
       int gt = 0, eq = 0;
-      for (int i = tid; i < c1; i += kNT) {
+      for (int i = tid; i < c1; i += NT) {
         const bool earlier = int(s_list[i] >> 21) < u;
         const uint32_t low = s_list[i] & 0x1FFFFFu;
         gt += int(earlier && low > tl);
         eq += int(earlier && low == tl);
       }
-      base += block_sum(gt, s_red);
-      tie0 = kr3 > 0 ? block_sum(eq, s_red) : 0;
+      base += block_sum<NT>(gt, s_red);
+      tie0 = kr3 > 0 ? block_sum<NT>(eq, s_red) : 0;
       base += min(tie0, kr3);
     } else {
       // ---- overflow: digit 2 from a second row histogram ------------------------------
@@ -446,7 +464,7 @@ __global__ __launch_bounds__(kNT) void topk_coop_kernel(TopkArgs a, uint8_t *ws)
           eq += int((key[e] >> 10) == p2);
         }
       }, false);
-      const int above2 = block_sum(mode2 == 0 ? gt + eq : gt, s_red);
+      const int above2 = block_sum<NT>(mode2 == 0 ? gt + eq : gt, s_red);
       if (tid == 0) st(reinterpret_cast<uint32_t *>(&ui->above2), uint32_t(above2));
       if (mode2 == 1)
         append([&](uint32_t key) { return (key >> 10) == p2; });
@@ -461,23 +479,23 @@ __global__ __launch_bounds__(kNT) void topk_coop_kernel(TopkArgs a, uint8_t *ws)
         T = (p2 << 10) - 1u;
       } else if (mode2 == 1) {
         read_list(c2);
-        zero_lds(s_h, 1024);
+        zero_lds<NT>(s_h, 1024);
         __syncthreads();
-        for (int i = tid; i < c2; i += kNT) atomicAdd(&s_h[s_list[i] & 1023u], 1u);
+        for (int i = tid; i < c2; i += NT) atomicAdd(&s_h[s_list[i] & 1023u], 1u);
         __syncthreads();
         select(s_h, 1024, kr2);
         T = (p2 << 10) | uint32_t(s_sel[0]);
         kr3 = kr2 - s_sel[1];
         const uint32_t tl = T & 0x1FFFFFu;
         int g3 = 0, e3 = 0;
-        for (int i = tid; i < c2; i += kNT) {
+        for (int i = tid; i < c2; i += NT) {
           const bool earlier = int(s_list[i] >> 21) < u;
           const uint32_t low = s_list[i] & 0x1FFFFFu;
           g3 += int(earlier && low > tl);
           e3 += int(earlier && low == tl);
         }
-        base += block_sum(g3, s_red);
-        tie0 = block_sum(e3, s_red);
+        base += block_sum<NT>(g3, s_red);
+        tie0 = block_sum<NT>(e3, s_red);
         base += min(tie0, kr3);
       } else {
         read_hist(rs.h3, 1024);
@@ -493,8 +511,8 @@ __global__ __launch_bounds__(kNT) void topk_coop_kernel(TopkArgs a, uint8_t *ws)
             e3 += int(key[e] == T);
           }
         }, false);
-        g3 = block_sum(g3, s_red);
-        e3 = block_sum(e3, s_red);
+        g3 = block_sum<NT>(g3, s_red);
+        e3 = block_sum<NT>(e3, s_red);
         if (tid == 0) {
           st(reinterpret_cast<uint32_t *>(&ui->gt3), uint32_t(g3));
           st(reinterpret_cast<uint32_t *>(&ui->eq3), uint32_t(e3));
@@ -569,15 +587,16 @@ __global__ __launch_bounds__(kNT) void topk_coop_kernel(TopkArgs a, uint8_t *ws)
   if (solo) return;
 
   // ---- the row's last unit clears its record ------------------------------------------
+  if constexpr (SOLO) return;
   __syncthreads();
   if (tid == 0) s_last = add(&rs.depart, 1u) == uint32_t(nu - 1);
   __syncthreads();
   if (s_last) {
-    for (int b = tid; b < kBins; b += kNT) {
+    for (int b = tid; b < kBins; b += NT) {
       st(&rs.h1[b], 0u);
       st(&rs.h2[b], 0u);
     }
-    for (int b = tid; b < 1024; b += kNT) st(&rs.h3[b], 0u);
+    for (int b = tid; b < 1024; b += NT) st(&rs.h3[b], 0u);
     if (tid < 4) st(&rs.arrive[tid], 0u);
     if (tid == 4) st(&rs.nlist, 0u);
     if (tid == 5) st(&rs.depart, 0u);
@@ -609,6 +628,8 @@ void *topk_static_scratch(size_t *bytes) {
   return addr[dev];
 }
 
+constexpr int kCap = kNT * kKPL;  // keys a shared-row unit holds at once
+
 // Workgroups of the cooperative kernel for these rows: enough units of at most kCap
 // columns for rows of `width`, no more than the device holds at once (0: it cannot
 // run). Fewer workgroups also start sooner.
@@ -620,7 +641,7 @@ int topk_coop_grid(int num_cus, int rows, int width) {
     std::lock_guard<std::mutex> lock(mu);
     if (per_cu < 0) {
       int n = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, topk_coop_kernel, kNT, 0) != hipSuccess) n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, topk_reg_kernel<kNT, kKPL, false>, kNT, 0) != hipSuccess) n = 0;
       per_cu = n;
     }
     resident = per_cu * num_cus;
@@ -630,7 +651,14 @@ int topk_coop_grid(int num_cus, int rows, int width) {
 }
 
 hipError_t launch_topk_coop(const TopkArgs &a, void *scratch, int grid, hipStream_t stream) {
-  topk_coop_kernel<<<dim3(grid), kNT, 0, stream>>>(a, static_cast<uint8_t *>(scratch));
+  topk_reg_kernel<kNT, kKPL, false><<<dim3(grid), kNT, 0, stream>>>(a, static_cast<uint8_t *>(scratch));
+  return hipGetLastError();
+}
+
+int topk_solo_cap() { return 256 * 32; }
+
+hipError_t launch_topk_solo(const TopkArgs &a, hipStream_t stream) {
+  topk_reg_kernel<256, 32, true><<<dim3(a.rows), 256, 0, stream>>>(a, nullptr);
   return hipGetLastError();
 }
 

@@ -62,6 +62,26 @@ def test_topk_many_rows():
     np.testing.assert_array_equal(got, indexer.topk(L.astype(np.float64), None, ends, k))
 
 
+@pytest.mark.parametrize("width,k", [(8192, 2048), (3001, 64), (300, 256)])
+def test_topk_many_rows_in_registers(width, k):
+    # 1024 rows or more of at most 8192 columns: one 256-thread workgroup per row, keys
+    # in registers. Rows of every length class: empty, shorter than k, exactly k, k + 1,
+    # full; unaligned starts; heavy ties; all equal; -inf inside the range
+    rng = np.random.default_rng(width + k + 1)
+    rows = 1500
+    L = rng.standard_normal((rows, width)).astype(np.float32)
+    L[0::7] = np.round(L[0::7] * 2) / 2
+    L[1::7] = 0.5
+    L[2::7, : width // 3] = -np.inf
+    starts = rng.integers(0, 9, rows)
+    ends = rng.integers(0, width + 1, rows)
+    ends[3::11] = np.minimum(starts[3::11] + k, width)
+    ends[4::11] = np.minimum(starts[4::11] + k + 1, width)
+    ends[5::11] = width
+    ends[6::11] = starts[6::11]
+    np.testing.assert_array_equal(_run(L, starts, ends, k), indexer.topk(L.astype(np.float64), starts, ends, k))
+
+
 # ---- several workgroups per row (up to 256 rows of more than 65536 columns, 16-byte aligned)
 def _oracle(L, starts, ends, k):
     return indexer.topk(L.astype(np.float64), starts, ends, k)
