@@ -12,7 +12,7 @@ is 0. For them the bound is stated against the size of the terms instead:
 2^-11 * max_s A[t, s], with A[t, s] = sum_h |w| * k_scale * sum_d |q k| (the
 oracle's ``magnitude=True``). 2^-11 covers the matrix cores' accumulation error of
 a 128-term dot product, which ``tests/test_gpu_accumulation.py`` measures on
-adversarial sums and asserts to be below 2^-12. Every row with more valid keys is
+adversarial sums and asserts to be below 2^-11.75. Every row with more valid keys is
 held to the plain 2e-3 bound whether or not a magnitude array is passed.
 
 Top-k: index sets must match, except that an index in one set and not the other

@@ -1,18 +1,32 @@
 """The C ABI without a GPU: the library loads, exports every function include/idx.h
 declares, and its host-side checks reject bad arguments before any launch (each
-call here fails a check, so nothing reaches the device)."""
+call here fails a check, so nothing reaches the device).
+
+With IDX_TEST_LIB naming the ABI layer built for the host under AddressSanitizer and
+UndefinedBehaviorSanitizer (tests/host_asan, run by tests/test_host_asan.py), the same
+tests run against that build, and the tests at the end also pretend a gfx950 is present:
+every valid call then reaches exactly its kernel launchers (stand-ins that check the
+arguments the kernels rely on) and no rejected call reaches one."""
 
 import ctypes
 import os
 import re
 
 import pytest
-import torch
 
 from sparse_attention_indexer_mxfp4_amd import _abi
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "idx.h")
+HOST_LIB = os.environ.get("IDX_TEST_LIB")
+
+
+def _gpu_visible():
+    if HOST_LIB:
+        return False  # the host build reports no device unless a test asks for one
+    import torch
+
+    return torch.cuda.is_available()
 
 OK, NULL, SHAPE, STRIDE, FORMAT, WORKSPACE, LAUNCH, DEVICE = range(8)
 P = 0x10000  # an aligned, never-dereferenced stand-in address
@@ -20,6 +34,10 @@ P = 0x10000  # an aligned, never-dereferenced stand-in address
 
 @pytest.fixture(scope="module")
 def lib():
+    if HOST_LIB:
+        handle = ctypes.CDLL(HOST_LIB)
+        _abi._declare(handle)
+        return handle
     return _abi.lib()
 
 
@@ -36,6 +54,7 @@ def test_exports_every_declared_function(lib):
     assert sorted(names) == sorted(_abi.EXPORTS)
 
 
+@pytest.mark.skipif(bool(HOST_LIB), reason="the measurement library is not part of the ABI layer")
 def test_calibration_library_exports():
     # the measurement kernels bench.py reports beside the spec peaks (include/idx_calib.h)
     text = open(os.path.join(ROOT, "include", "idx_calib.h")).read()
@@ -316,7 +335,7 @@ def test_paged_prefill_checks(lib):
     assert _pf(width=0, out=None) == OK  # nothing to write, nothing launched
 
 
-@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path; a GPU is visible")
+@pytest.mark.skipif(_gpu_visible(), reason="checks the no-device path; a GPU is visible")
 def test_paged_prefill_empty_table_passes_host_checks(lib):
     # an fp8 chunk with no block-table entries (NULL table, max_blocks 0) but rows that
     # end past 0 is a valid call: every column is -inf. It must pass the host checks and
@@ -328,8 +347,84 @@ def test_paged_prefill_empty_table_passes_host_checks(lib):
     assert f(ctypes.byref(_cache(fmt=1)), P, P, P, P, None, 0, 64, 64, P, 512, 512, None) == DEVICE
 
 
-@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path; a GPU is visible")
+@pytest.mark.skipif(_gpu_visible(), reason="checks the no-device path; a GPU is visible")
 def test_valid_call_without_device_reports_device_error(lib):
     # arguments pass every host check, so the call reaches the device query, which
     # fails here because this machine has no GPU; nothing is launched
     assert _topk(lib) == DEVICE
+
+
+# ---- host build only: a pretend gfx950 behind the ABI layer ---------------------------
+
+host_only = pytest.mark.skipif(not HOST_LIB, reason="needs the host build of the ABI layer (tests/host_asan)")
+
+
+@pytest.fixture
+def device(lib):
+    lib.idx_host_set_device(1)
+    yield lib
+    lib.idx_host_set_device(0)
+
+
+def _launches(lib, call, what=""):
+    """(status, launches) of one call, with no launcher check failing."""
+    n0, v0 = lib.idx_host_launches(), lib.idx_host_violations()
+    s = call()
+    assert lib.idx_host_violations() == v0, f"{what}: a launcher was reached with arguments its kernels cannot use"
+    return s, lib.idx_host_launches() - n0
+
+
+@host_only
+def test_host_valid_calls_reach_their_launchers(device):
+    lib = device
+    c8, c4 = _cache(), _cache(fmt=1)
+    kn, qr = lib.idx_k_norm_rope_store, lib.idx_q_rope_quant
+    calls = {
+        "mqa": lambda: _mqa(lib),
+        "paged fp8": lambda: _paged(lib),
+        "paged mxfp4": lambda: _paged(lib, cache=c4, qsc=P),
+        "paged per-row lengths": lambda: _paged(lib, per_row=1, nn=2),
+        "topk": lambda: _topk(lib),
+        "topk many rows": lambda: _topk(lib, rows=300, ws=None, wsb=0),
+        "topk noalloc": lambda: lib.idx_topk_noalloc(P, 1000, 4, 1000, None, P, 16, P, 16, None),
+        "k store": lambda: lib.idx_k_store(ctypes.byref(c8), P, 0, 128, P, 10, None),
+        "q quant fp8": lambda: lib.idx_q_quant(P, 0, 128, 4, 1, 128, 0, P, None, None),
+        "q quant mxfp4": lambda: lib.idx_q_quant(P, 0, 128, 4, 1, 128, 1, P, P, None),
+        "k norm rope store": lambda: kn(ctypes.byref(c8), P, 0, 128, P, P, 16, 64, P, 1e-6, P, 10, None),
+        "q rope quant": lambda: qr(P, 0, 128, P, P, 16, 64, P, 1, 1.0, 4, 1, 128, 0, P, None, P, None),
+        "slots": lambda: lib.idx_topk_to_slots(P, 8, 4, 8, None, 1, 2, None, P, 4, 4, 16, P, P, None, None),
+        "block max": lambda: lib.idx_paged_mqa_logits_block_max(ctypes.byref(c8), P, None, P, P, 0, P, 8, 8, 4, 1,
+                                                                64, P, 512, 512, None, P, 32, 16, None, 0, None),
+        "gather": lambda: lib.idx_paged_mqa_logits_gather(ctypes.byref(c8), P, None, P, P, 0, P, 8, 8, 4, 1, 64, P,
+                                                          8, 8, 64, 1, P, 512, P, None),
+        "candidate blocks": lambda: lib.idx_candidate_blocks(P, 32, 4, 32, P, 16, 8, P, 8, P, WS4, None),
+        "candidate mask": lambda: lib.idx_apply_candidate_mask(P, 512, 4, 512, P, P, 8, 8, 16, 1, None),
+        "remap": lambda: lib.idx_remap_compact_topk(P, 16, 4, 16, P, 8, 8, 16, 1, None),
+    }
+    pf = lib.idx_paged_prefill_logits
+    calls.update({
+        "prefill fp8 pages": lambda: pf(ctypes.byref(c8), P, None, P, P, P, 8, 64, 64, P, 512, 512, None),
+        "prefill mxfp4 pages": lambda: pf(ctypes.byref(c4), P, P, P, P, P, 8, 64, 64, P, 512, 512, None),
+        "prefill mxfp4 pages, 128 heads": lambda: pf(ctypes.byref(c4), P, P, P, P, P, 8, 64, 128, P, 512, 512,
+                                                     None),
+        # no block-table entries: the fp8 chunk must take the paged kernel with no key
+        # to read (a NULL table is valid then), never the contiguous one
+        "prefill fp8, empty table": lambda: pf(ctypes.byref(c8), P, None, P, P, None, 0, 64, 64, P, 512, 512, None),
+        "prefill mxfp4, empty table": lambda: pf(ctypes.byref(c4), P, P, P, P, None, 0, 64, 64, P, 512, 512, None),
+    })
+    for name, call in calls.items():
+        s, n = _launches(lib, call, name)
+        assert s == OK, (name, s)
+        assert n >= 1, f"{name}: nothing launched"
+
+
+@host_only
+@pytest.mark.parametrize("check,launches", [
+    (test_mqa_logits_checks, 0), (test_paged_checks, 0), (test_topk_checks, 1),
+    (test_k_store_and_q_quant_checks, 0), (test_fused_producer_checks, 0), (test_topk_to_slots_checks, 0),
+    (test_two_level_checks, 0), (test_paged_prefill_checks, 0)])
+def test_host_rejected_calls_launch_nothing(device, check, launches):
+    # the argument checks above, now with a device present: every rejected or empty call
+    # returns before any launcher (test_topk_checks holds one valid call, 300 rows)
+    s, n = _launches(device, lambda: check(device), check.__name__)
+    assert n == launches, check.__name__
