@@ -8,8 +8,9 @@ workloads, with the dominant kernel's roofline fraction and the CPU oracle besid
 Default: the headline is the paged fp8 MTP decode step (128 sequences x 2 rows,
 context lengths log-uniform on [4096, 65536], 64 heads, logits width 65536,
 top-2048), the largest decode workload; the line also carries the fp8 decode
-(B = 32), the fp8 prefill chunk (8192 x 8192) and the MXFP4 decode (B = 64) as
-sub-objects under "configs", each with its own roofline and CPU oracle baseline, and
+(B = 32), the fp8 prefill chunk (8192 x 8192), the MXFP4 decode (B = 64) and the
+MXFP4 prefill chunk read off the paged cache (8192 x 8192) as sub-objects under
+"configs", each with its own roofline and CPU oracle baseline, and
 the ceilings measured on this GPU (streaming copy / read, fp8 / fp4 matrix loops)
 under "calibration". ``--config N`` prints one workload's line instead (1-5: the five
 workloads; 6: the MXFP4 prefill chunk read off the paged cache). Inputs live in HBM
@@ -303,7 +304,7 @@ def calibration(torch):
 # ------------------------------------------------------------------------------------
 # GPU
 # ------------------------------------------------------------------------------------
-SUB_CONFIGS = (2, 4, 5)
+SUB_CONFIGS = (2, 4, 5, 6)
 
 
 def main():
