@@ -246,6 +246,77 @@ __device__ void finish_row(Smem<NT> &sm, KeyAt key_at, int n, int k, int32_t *ou
   }
 }
 
+// The cached walks take KS sub-steps of 64 * B keys per wave step: in sub-step j lane L
+// holds the B consecutive columns base + 64 B j + B L + e, e < B, and a per-lane bit
+// mask marks keys (bit B j + e), so a step of 64 B KS keys costs two lane scans instead
+// of KS, and stores loop over set bits only (few keys of a row are selected).
+constexpr int kSubSteps = 4;
+
+// Output slots of the keys whose bits are set in `sel`, in column order (sub-step,
+// then lane, then column): each lane's first slot per sub-step comes from lane scans
+// of packed per-sub-step counts (16-bit fields: a sub-step holds at most 64 B keys).
+// Writes the columns (relative to the row start) below k; returns pos advanced by the
+// wave's selected keys.
+template <int B, int KS>
+__device__ __forceinline__ int emit_bits(uint32_t sel, int base, int lane, int pos, int k, int32_t *out) {
+  static_assert(B * KS <= 32 && KS % 2 == 0, "bit layout");
+  constexpr uint32_t kMask = (1u << B) - 1u;
+  if (__ballot(sel != 0u) == 0ull) return pos;
+  int first[KS], total[KS];
+#pragma unroll
+  for (int j = 0; j < KS; j += 2) {
+    const uint32_t c0 = uint32_t(__builtin_popcount((sel >> (B * j)) & kMask));
+    const uint32_t c1 = uint32_t(__builtin_popcount((sel >> (B * (j + 1))) & kMask));
+    const uint32_t inc = uint32_t(wave_incl_scan(int(c0 | (c1 << 16))));
+    const uint32_t tot = uint32_t(__builtin_amdgcn_readlane(int(inc), 63));
+    first[j] = int((inc & 0xFFFFu) - c0);
+    first[j + 1] = int((inc >> 16) - c1);
+    total[j] = int(tot & 0xFFFFu);
+    total[j + 1] = int(tot >> 16);
+  }
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    uint32_t m = (sel >> (B * j)) & kMask;
+    int p = pos + first[j];
+    const int col = base + 64 * B * j + B * lane;
+    while (m != 0u) {
+      const int e = __builtin_ctz(m);
+      m &= m - 1u;
+      if (p < k) out[p] = col + e;
+      ++p;
+    }
+    pos += total[j];
+  }
+  return pos;
+}
+
+// Of the keys equal to T (bits of `eq`, same layout), the ones whose rank among the
+// row's ties in column order is below kr; eq_run counts the ties met before this step.
+template <int B, int KS>
+__device__ __forceinline__ uint32_t take_ties(uint32_t eq, int kr, int &eq_run) {
+  constexpr uint32_t kMask = (1u << B) - 1u;
+  uint32_t take = 0u;
+  if (__ballot(eq != 0u) == 0ull) return take;
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    const uint32_t ej = (eq >> (B * j)) & kMask;
+    if (__ballot(ej != 0u) != 0ull) {
+      const int neq = __builtin_popcount(ej);
+      const int inc = wave_incl_scan(neq);
+      int r = eq_run + inc - neq;
+      uint32_t m = ej;
+      while (m != 0u) {
+        const int e = __builtin_ctz(m);
+        m &= m - 1u;
+        take |= uint32_t(r < kr) << (B * j + e);
+        ++r;
+      }
+      eq_run += __builtin_amdgcn_readlane(inc, 63);
+    }
+  }
+  return take;
+}
+
 // Phases 3 to 5 for a row whose keys sit in LDS, padded with zero keys up to a whole
 // step (a zero key ranks below every real one: -inf maps to bin 3). Each lane holds
 // four consecutive keys per step, read with one 16-byte load, so a step needs no
@@ -268,34 +339,37 @@ __device__ void finish_cached(Smem<NT> &sm, const uint32_t *keys, int n, int k, 
   // ---- phase 3 ----------------------------------------------------------------------
   for (int i = tid; i < kBins; i += NT) sm.hist[i] = 0u;
   int above = 0, match = 0;
-  for (int base = lo; base < hi; base += kStep) {
-    const v4i kv = *reinterpret_cast<const v4i *>(keys + base + 4 * lane);
-    int nc = 0;
+  for (int base = lo; base < hi; base += kStep * kSubSteps) {
+    uint32_t cm = 0u;  // keys of bin d1
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t key = uint32_t(kv[e]);
-      above += int(key > top);
-      nc += int((key >> 21) == d1);
-    }
-    match += nc;
-    if (!whole_bin) {
-      const int incl = wave_incl_scan(nc);
-      const int tot = __builtin_amdgcn_readlane(incl, 63);
-      if (tot != 0) {
-        int slot = 0;
-        if (lane == 0) slot = atomicAdd(&sm.ncand, tot);
-        slot = __builtin_amdgcn_readfirstlane(slot) + incl - nc;
+    for (int j = 0; j < kSubSteps; ++j) {
+      if (base + j * kStep < hi) {
+        const v4i kv = *reinterpret_cast<const v4i *>(keys + base + j * kStep + 4 * lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t key = uint32_t(kv[e]);
-          if ((key >> 21) == d1) {
-            // the list holds the bin's c1 <= kCand keys; only padding could add more,
-            // and only for a row whose k-th key sorts below -inf (a NaN)
-            atomicAdd(&sm.hist2[(key >> 10) & uint32_t(kBins - 1)], 1u);
-            if (slot < Cfg<NT>::kCand) sm.cand[slot] = (uint32_t(wave) << 21) | (key & 0x1FFFFFu);
-            ++slot;
-          }
+          above += int(key > top);
+          cm |= uint32_t((key >> 21) == d1) << (4 * j + e);
         }
+      }
+    }
+    const int nc = __builtin_popcount(cm);
+    match += nc;
+    if (!whole_bin && __ballot(nc != 0) != 0ull) {
+      const int incl = wave_incl_scan(nc);
+      const int tot = __builtin_amdgcn_readlane(incl, 63);
+      int slot = 0;
+      if (lane == 0) slot = atomicAdd(&sm.ncand, tot);
+      slot = __builtin_amdgcn_readfirstlane(slot) + incl - nc;
+      while (cm != 0u) {
+        const int b = __builtin_ctz(cm);
+        cm &= cm - 1u;
+        const uint32_t key = keys[base + (b >> 2) * kStep + 4 * lane + (b & 3)];
+        // the list holds the bin's c1 <= kCand keys; only padding could add more,
+        // and only for a row whose k-th key sorts below -inf (a NaN)
+        atomicAdd(&sm.hist2[(key >> 10) & uint32_t(kBins - 1)], 1u);
+        if (slot < Cfg<NT>::kCand) sm.cand[slot] = (uint32_t(wave) << 21) | (key & 0x1FFFFFu);
+        ++slot;
       }
     }
   }
@@ -341,41 +415,22 @@ __device__ void finish_cached(Smem<NT> &sm, const uint32_t *keys, int n, int k, 
   before_wave(sm, wave, lane, gt_before, eq_before);
   int pos = gt_before + min(eq_before, kr);
   int eq_run = eq_before;
-  for (int base = lo; base < hi; base += kStep) {
-    const v4i kv = *reinterpret_cast<const v4i *>(keys + base + 4 * lane);
-    bool sel[4];
-    int neq = 0;
+  for (int base = lo; base < hi; base += kStep * kSubSteps) {
+    uint32_t sel = 0u, eq = 0u;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sel[e] = uint32_t(kv[e]) > T;
-      neq += int(uint32_t(kv[e]) == T);
-    }
-    if (__ballot(neq != 0) != 0ull) {
-      // ties in column order: rank = ties before this step + ties in earlier lanes +
-      // ties in this lane's earlier columns; the first kr ranks are taken
-      const int incl = wave_incl_scan(neq);
-      int r = eq_run + incl - neq;
+    for (int j = 0; j < kSubSteps; ++j) {
+      if (base + j * kStep < hi) {
+        const v4i kv = *reinterpret_cast<const v4i *>(keys + base + j * kStep + 4 * lane);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (uint32_t(kv[e]) == T) {
-          sel[e] = r < kr;
-          ++r;
+        for (int e = 0; e < 4; ++e) {
+          sel |= uint32_t(uint32_t(kv[e]) > T) << (4 * j + e);
+          eq |= uint32_t(uint32_t(kv[e]) == T) << (4 * j + e);
         }
       }
-      eq_run += __builtin_amdgcn_readlane(incl, 63);
     }
-    const int ns = int(sel[0]) + int(sel[1]) + int(sel[2]) + int(sel[3]);
-    const int incl = wave_incl_scan(ns);
-    int p = pos + incl - ns;
-    const int col = base + 4 * lane;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (sel[e]) {
-        if (p < k) out[p] = col + e;
-        ++p;
-      }
-    }
-    pos += __builtin_amdgcn_readlane(incl, 63);
+    // ties in column order: the first kr of the row's ties are taken
+    if (kr > 0) sel |= take_ties<4, kSubSteps>(eq, kr, eq_run);
+    pos = emit_bits<4, kSubSteps>(sel, base, lane, pos, k, out);
   }
 }
 
@@ -403,31 +458,33 @@ __device__ void finish_half(Smem<NT> &sm, uint16_t *top16, const float *lr, int 
   // ---- phase 3: counts above the bin, columns of the bin's keys ----------------------
   for (int i = tid; i < kBins; i += NT) sm.hist[i] = 0u;
   int above = 0, match = 0;
-  for (int base = lo; base < hi; base += kStep) {
-    const v4i raw = *reinterpret_cast<const v4i *>(top16 + base + 8 * lane);
-    uint32_t inbin = 0;
+  for (int base = lo; base < hi; base += kStep * kSubSteps) {
+    uint32_t inbin = 0u;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t t = (uint32_t(raw[e >> 1]) >> (16 * (e & 1))) & 0xFFFFu;
-      above += int((t >> 5) > d1);
-      inbin |= uint32_t((t >> 5) == d1) << e;
+    for (int j = 0; j < kSubSteps; ++j) {
+      if (base + j * kStep < hi) {
+        const v4i raw = *reinterpret_cast<const v4i *>(top16 + base + j * kStep + 8 * lane);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t t = (uint32_t(raw[e >> 1]) >> (16 * (e & 1))) & 0xFFFFu;
+          above += int((t >> 5) > d1);
+          inbin |= uint32_t((t >> 5) == d1) << (8 * j + e);
+        }
+      }
     }
     const int nc = __builtin_popcount(inbin);
     match += nc;
-    if (!whole_bin) {
+    if (!whole_bin && __ballot(nc != 0) != 0ull) {
       const int incl = wave_incl_scan(nc);
       const int tot = __builtin_amdgcn_readlane(incl, 63);
-      if (tot != 0) {
-        int slot = 0;
-        if (lane == 0) slot = atomicAdd(&sm.ncand, tot);
-        slot = __builtin_amdgcn_readfirstlane(slot) + incl - nc;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if ((inbin >> e) & 1u) {
-            if (slot < kCand) sm.cand[slot] = uint32_t(base + 8 * lane + e);
-            ++slot;
-          }
-        }
+      int slot = 0;
+      if (lane == 0) slot = atomicAdd(&sm.ncand, tot);
+      slot = __builtin_amdgcn_readfirstlane(slot) + incl - nc;
+      while (inbin != 0u) {
+        const int b = __builtin_ctz(inbin);
+        inbin &= inbin - 1u;
+        if (slot < kCand) sm.cand[slot] = uint32_t(base + (b >> 3) * kStep + 8 * lane + (b & 7));
+        ++slot;
       }
     }
   }
@@ -487,40 +544,22 @@ __device__ void finish_half(Smem<NT> &sm, uint16_t *top16, const float *lr, int 
   before_wave(sm, wave, lane, gt_before, eq_before);
   int pos = gt_before + min(eq_before, kr);
   int eq_run = eq_before;
-  for (int base = lo; base < hi; base += kStep) {
-    const v4i raw = *reinterpret_cast<const v4i *>(top16 + base + 8 * lane);
-    uint32_t sel = 0, eq = 0;  // bit e: column base + 8 lane + e
+  for (int base = lo; base < hi; base += kStep * kSubSteps) {
+    uint32_t sel = 0u, eq = 0u;  // bit 8 j + e: column base + kStep j + 8 lane + e
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t t = (uint32_t(raw[e >> 1]) >> (16 * (e & 1))) & 0xFFFFu;
-      sel |= uint32_t(t > tp) << e;
-      eq |= uint32_t(t == tp) << e;
-    }
-    if (__ballot(eq != 0u) != 0ull) {
-      const int neq = __builtin_popcount(eq);
-      const int incl = wave_incl_scan(neq);
-      int r = eq_run + incl - neq;
+    for (int j = 0; j < kSubSteps; ++j) {
+      if (base + j * kStep < hi) {
+        const v4i raw = *reinterpret_cast<const v4i *>(top16 + base + j * kStep + 8 * lane);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if ((eq >> e) & 1u) {
-          sel |= uint32_t(r < kr) << e;
-          ++r;
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t t = (uint32_t(raw[e >> 1]) >> (16 * (e & 1))) & 0xFFFFu;
+          sel |= uint32_t(t > tp) << (8 * j + e);
+          eq |= uint32_t(t == tp) << (8 * j + e);
         }
       }
-      eq_run += __builtin_amdgcn_readlane(incl, 63);
     }
-    const int ns = __builtin_popcount(sel);
-    const int incl = wave_incl_scan(ns);
-    int p = pos + incl - ns;
-    const int col = base + 8 * lane;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if ((sel >> e) & 1u) {
-        if (p < k) out[p] = col + e;
-        ++p;
-      }
-    }
-    pos += __builtin_amdgcn_readlane(incl, 63);
+    if (kr > 0) sel |= take_ties<8, kSubSteps>(eq, kr, eq_run);
+    pos = emit_bits<8, kSubSteps>(sel, base, lane, pos, k, out);
   }
 }
 
@@ -571,10 +610,12 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
   if ((reinterpret_cast<uintptr_t>(lr) & 15) == 0) {
     const buffer_rsrc rs = make_rsrc(lr, uint32_t(n) * 4u);
     constexpr int kGroups = kUnroll / 4;
-    for (int base = 0; base < n; base += kUnroll * NT) {
-      v4i x[kGroups];
+    constexpr int kBatch = kUnroll * NT;  // keys per batch of loads
+    auto issue = [&](v4i (&x)[kGroups], int base) {
 #pragma unroll
       for (int u = 0; u < kGroups; ++u) x[u] = buffer_load16(rs, uint32_t(base + (u * NT + tid) * 4) * 4u);
+    };
+    auto consume = [&](const v4i (&x)[kGroups], int base) {
 #pragma unroll
       for (int u = 0; u < kGroups; ++u) {
         const int i = base + (u * NT + tid) * 4;
@@ -592,6 +633,16 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
           }
         }
       }
+    };
+    // two register sets: the next batch's loads are in flight while this one is used
+    // (a row longer than one batch no longer pays a memory round trip per batch)
+    v4i xa[kGroups], xb[kGroups];
+    issue(xa, 0);
+    for (int base = 0; base < n; base += 2 * kBatch) {
+      if (base + kBatch < n) issue(xb, base + kBatch);
+      consume(xa, base);
+      if (base + 2 * kBatch < n) issue(xa, base + 2 * kBatch);
+      if (base + kBatch < n) consume(xb, base + kBatch);
     }
   } else {
     for (int base = 0; base < n; base += kUnroll * NT) {

@@ -236,19 +236,22 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a, uint8_t *ws) {
 
   uint32_t kr4[kSteps][4];
   // keys of the pass starting at column cb: 0 (no key) outside [st0, whi)
+  // (the raw bits land in kr4 and are converted in place, so a pass needs no second
+  // set of registers)
   auto load_pass = [&](int cb) {
-    v4i x[kSteps];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       const int c = cb + s * 256 + 4 * lane;
-      x[s] = c < whi ? buffer_load16(rsrc, uint32_t(c) * 4u) : v4i{0, 0, 0, 0};
+      const v4i x = c < whi ? buffer_load16(rsrc, uint32_t(c) * 4u) : v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kr4[s][e] = uint32_t(x[e]);
     }
 #pragma unroll
     for (int s = 0; s < kSteps; ++s)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int c = cb + s * 256 + 4 * lane + e;
-        kr4[s][e] = (c >= st0 && c < whi) ? order_key(__int_as_float(x[s][e])) : 0u;
+        kr4[s][e] = (c >= st0 && c < whi) ? order_key(__uint_as_float(kr4[s][e])) : 0u;
       }
   };
   // fn(keys of 4 consecutive columns, first column) over the wave's segment in column
