@@ -21,7 +21,8 @@
 // ones left, about 16 significant bits together), so it too runs on the fp8 matrix
 // cores: one MFMA per 16-key group covers the 2 rows x 4 parts of a wave.
 //
-// Work split: a workgroup owns 8 query rows (two per wave) and one key split. Each
+// Work split: a workgroup owns 8 query rows (two per wave; 4 rows, one per wave, with
+// more than 64 heads) and one key split. Each
 // wave keeps its rows' queries in registers as MFMA A operands (16 heads per tile,
 // all 128 channels in one 16x16x128 fp8 MFMA), and the workgroup streams K through
 // two LDS buffers shared by its four waves in stages of two 64-key chunks (a stage's
@@ -45,8 +46,9 @@ namespace idx {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kRowsPerWave = 2;
-constexpr int kRowsPerWG = kWaves * kRowsPerWave;
+// query rows per wave: two, or one with 128 heads (eight head tiles of queries,
+// weights and scores for two rows do not fit a wave's 256 registers)
+constexpr int rows_per_wave(int ht) { return ht > 4 ? 1 : 2; }
 constexpr int kChunk = 64;   // keys scored at once: key L of a chunk ends in lane L
 constexpr int kSub = 2;      // chunks per LDS stage (one barrier per stage)
 constexpr int kStage = kChunk * kSub;
@@ -55,6 +57,8 @@ constexpr int kKeyStride = 144;  // LDS bytes per key / query row: 128 + 16 of p
 
 template <int HT, bool PAGED>
 __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int split_keys) {
+  constexpr int kRowsPerWave = rows_per_wave(HT);
+  constexpr int kRowsPerWG = kWaves * kRowsPerWave;
   __shared__ __attribute__((aligned(16))) uint8_t sk[2][kStage * kKeyStride];
   __shared__ float ss[2][kStage];
   __shared__ __attribute__((aligned(16))) uint8_t sl[kWaves][16 * kKeyStride];  // qt parts, A-operand rows
@@ -168,9 +172,9 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
       *reinterpret_cast<uint16_t *>(&sl[wave][(rr * 4 + part) * kKeyStride + qoff]) = uint16_t(e);
     }
   }
-  // rows 8..15 of the qt operand tile stay zero
-  for (int i = lane; i < 8 * kKeyStride / 16; i += 64)
-    *reinterpret_cast<v4i *>(&sl[wave][8 * kKeyStride + 16 * i]) = v4i{0, 0, 0, 0};
+  // the qt operand tile's rows past the wave's row parts stay zero
+  for (int i = lane; i < (16 - 4 * kRowsPerWave) * kKeyStride / 16; i += 64)
+    *reinterpret_cast<v4i *>(&sl[wave][4 * kRowsPerWave * kKeyStride + 16 * i]) = v4i{0, 0, 0, 0};
   __syncthreads();
   v8i la;  // A operand of the qt MFMA: row m = 4 * (row in wave) + part
   {
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
       kb[kg] = cat(*reinterpret_cast<const v4i *>(kp), *reinterpret_cast<const v4i *>(kp + 64));
     }
     float part[kRowsPerWave][4];  // sum over this lane's heads of w * |S|, per key group
-    float lin[4];                 // qt . k for row g of the wave (g < 2), before the 2^e scale
+    float lin[4];                 // qt . k for row g of the wave (g < rows per wave), before the 2^e scale
     v4f sv[2][kRowsPerWave][HT];
     v4f lv[2];
 #pragma unroll
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
       for (int rr = 0; rr < kRowsPerWave; ++rr) part[rr][kg] = acc[rr];
       __builtin_amdgcn_sched_barrier(0);
     }
-    // lane L: |S| sums for key L of each row; qt . k for key L of rows 0 and 1
+    // lane L: |S| sums for key L of each row; qt . k for key L of each row
     transpose4(lin);
     const int col = c + lane;
     const float sc = 0.5f * ss[buf][sub * kChunk + lane];
@@ -365,14 +369,15 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
 }  // namespace
 
 hipError_t launch_mqa_logits(const MqaArgs &a, int num_cus, hipStream_t stream) {
-  const int tiles = (a.M + kRowsPerWG - 1) / kRowsPerWG;
+  const int ht = (a.H + 15) / 16;
+  const int rows_wg = kWaves * rows_per_wave(ht <= 4 ? 4 : 8);
+  const int tiles = (a.M + rows_wg - 1) / rows_wg;
   const int nchunks = (a.N + kChunk - 1) / kChunk;
   int splits = (4 * num_cus + tiles - 1) / tiles;
   splits = max(1, min(splits, nchunks));
   const int split_keys = ((nchunks + splits - 1) / splits) * kChunk;
   splits = (a.N + split_keys - 1) / split_keys;
   const dim3 grid(tiles, splits);
-  const int ht = (a.H + 15) / 16;
   if (a.paged) {
     if (ht <= 1)
       mqa_logits_fp8_kernel<1, true><<<grid, 256, 0, stream>>>(a, split_keys);
