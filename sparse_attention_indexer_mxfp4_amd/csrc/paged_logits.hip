@@ -150,10 +150,19 @@ __global__ __launch_bounds__(64) void pool_length_kernel(PagedArgs a) {
   if (lane == 0) a.row_end_out[r] = last < 0 ? 0 : last * bs + min(bs, e - (blk << bsh));
 }
 
+// Three waves per SIMD where one row's registers fit a third of the register file
+// (168): one row with at most 64 heads, except the fp8 gathered walk, which would
+// spill; otherwise the compiler may use them all.
+template <int FMT, int HT, int NR, bool GATHER>
+constexpr int waves_per_simd() {
+  return NR == 1 && (HT <= 2 || (HT == 4 && !(FMT == 0 && GATHER))) ? 3 : 1;
+}
+
 // GATHER: each query row walks its own candidate pool (NR = 1, one "sequence" per
 // row); otherwise the dense walk over whole sequences, NR = next_n rows each.
 template <int FMT, int HT, int NR, bool GATHER>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NR == 1 ? 3 : 1))) void paged_logits_kernel(PagedArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<FMT, HT, NR, GATHER>())))
+void paged_logits_kernel(PagedArgs a) {
   extern __shared__ int s_lds[];  // pref[S + 1], len[S] (+ end[S] for the gather walk)
   __shared__ int s_scan[kThreads / 64];
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[FMT == 0 ? kThreads / 64 : 1][FMT == 0 ? kChunk * kTileStride : 16];
