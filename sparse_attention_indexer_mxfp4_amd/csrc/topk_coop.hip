@@ -256,7 +256,8 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a, uint8_t *ws) {
   };
   // fn(keys of 4 consecutive columns, first column) over the wave's segment in column
   // order, each lane holding 4 consecutive columns of a step; loads again only when the
-  // segment does not fit the registers
+  // segment does not fit the registers. Steps past the segment's end hold no key and
+  // are skipped (a short causal row fills a few of its steps).
   auto walk = [&](auto &&fn, bool load_first) {
     for (int cb = wlo; cb < whi; cb += kWaveCap) {
       if (load_first || !single) load_pass(cb);
@@ -264,6 +265,7 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a, uint8_t *ws) {
       // ahead of the first and hold them all in registers
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
+        if (cb + s * 256 >= whi) break;
         fn(kr4[s], cb + s * 256 + 4 * lane);
         __builtin_amdgcn_sched_barrier(0);
       }
