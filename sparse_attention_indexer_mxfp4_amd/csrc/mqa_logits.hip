@@ -53,7 +53,9 @@ constexpr int kChunk = 64;   // keys scored at once: key L of a chunk ends in la
 constexpr int kSub = 2;      // chunks per LDS stage (one barrier per stage)
 constexpr int kStage = kChunk * kSub;
 constexpr int kDepth = 2;  // K stages requested ahead of the one being scored
-constexpr int kKeyStride = 144;  // LDS bytes per key / query row: 128 + 16 of padding against bank conflicts
+constexpr int kKeyStride = 160;  // LDS bytes per key / query row: 128 + 32 of padding (rocprofv3
+                                  // counts no LDS bank conflicts at 160, 8.5 M cycles at 144, 176
+                                  // or 208 and 25 M at 128 per 8192x8192 chunk)
 
 template <int HT, bool PAGED>
 __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int split_keys) {
