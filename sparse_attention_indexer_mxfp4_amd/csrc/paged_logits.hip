@@ -67,7 +67,8 @@ constexpr int kMinChunksPerWave = 2;
 // single rows, where a third buffer would cost a wave per SIMD.
 template <int FMT, int NR>
 constexpr int ring_depth() { return NR == 1 ? 2 : 3; }
-constexpr int kTileStride = 144;  // LDS bytes per key row of a wave's fp8 tile (128 + 16 against bank conflicts)
+constexpr int kTileStride = 160;  // LDS bytes per key row of a wave's fp8 tile (128 + 32: rocprofv3 counts no
+                                  // bank conflicts at 160, 1.4 M cycles per MTP step at 144)
 
 // largest b in [0, B) with pref[b] <= u (pref[B] > u)
 __device__ __forceinline__ int find_seq(const int *pref, int B, int u) {
