@@ -222,3 +222,51 @@ def test_topk_aligned_rows(rows, width, k):
     ends[8] = starts[8] + 257
     got = _run(L, starts, ends, k)
     np.testing.assert_array_equal(got, indexer.topk(L.astype(np.float64), starts, ends, k))
+
+
+def _long_rows(rng, rows, width, k):
+    """Rows of up to 65536 keys: lengths from 0 to the width (log-spread, with the key
+    cache's size and the k-boundaries among them), ties across the middle of a row, a
+    row's best keys all in one half, -inf over a half, signed zeros."""
+    L = rng.standard_normal((rows, width)).astype(np.float32)
+    lens = np.exp(rng.uniform(np.log(1), np.log(width), rows)).astype(np.int64)
+    special = np.minimum([width, width - 1, 32768, 32769, 8192, 8193, 2 * k + 8, 2 * k + 9, k, k + 1, 0, 1], width)
+    m = min(len(special), rows - 6)
+    lens[6:6 + m] = special[:m]
+    L[0] = 0.75  # every key ties: the k lowest columns
+    L[1] = np.round(L[1] * 2) / 2  # heavy ties
+    half = width // 2
+    L[2, half:] += 8.0  # the row's best keys all in the second half
+    L[3, :half] += 8.0  # ... all in the first half
+    L[4, :half] = -np.inf
+    L[5, ::2] = -0.0
+    L[5, 1::2] = 0.0
+    lens[:6] = width
+    return L, lens
+
+
+@pytest.mark.parametrize("rows,width,k", [(12, 30000, 2048), (40, 65536, 512), (129, 40000, 2048),
+                                          (256, 65536, 2048)])
+def test_topk_long_rows(rows, width, k):
+    # decode-shaped steps: up to 256 rows of up to 65536 keys, rows longer than the key
+    # cache keeping 16-bit prefixes; unaligned starts take the unaligned read
+    rng = np.random.default_rng(rows + width + k)
+    L, lens = _long_rows(rng, rows, width, k)
+    starts = np.zeros(rows, np.int64)
+    starts[6::9] = 3
+    ends = np.minimum(starts + lens, width)
+    got = _run(L, starts, ends, k)
+    np.testing.assert_array_equal(got, indexer.topk(L.astype(np.float64), starts, ends, k))
+
+
+def test_topk_kernels_alternate_on_one_workspace():
+    # the one-workgroup and several-workgroups kernels alternate on the same workspace,
+    # which the latter must leave clear
+    rng = np.random.default_rng(11)
+    for rows, width, k in [(256, 65536, 2048), (8, 70000, 2048), (40, 50000, 2048), (8, 131072, 512),
+                           (256, 60000, 1024)]:
+        L, lens = _long_rows(rng, rows, width, k)
+        ends = np.minimum(lens, width)
+        got = _run(L, None, ends, k)
+        np.testing.assert_array_equal(got, indexer.topk(L.astype(np.float64), None, ends, k),
+                                      err_msg=f"rows {rows} width {width} k {k}")
