@@ -113,10 +113,31 @@ def idx_paged_mqa_logits(pool: torch.Tensor, fmt: int, page_size: int, q: torch.
     q_scale [B, next_n, H] int32 (MXFP4) or None, w [B*next_n, H] f32, context_lens [B] (or
     [B*next_n] with ctx_per_row) int32, block_table [B, max_blocks] int32.
     Returns (logits [B*next_n, width] f32, row_end [B*next_n] int32)."""
-    logits, row_end_out, _ = idx_paged_mqa_logits_block_max(
-        pool, fmt, page_size, q, q_scale, w, context_lens, block_table, width, 0, ctx_per_row, logits, row_end_out,
-        None, workspace)
+    cache = _paged_inputs(pool, fmt, page_size, q, q_scale, w, context_lens, block_table)
+    B, next_n, H = q.shape[:3]
+    logits, row_end_out = _paged_outputs(q, B * next_n, width, logits, row_end_out)
+    lib = _abi.lib()
+    workspace, ws_bytes = _paged_workspace(lib, cache, B, next_n, H, q.device, workspace)
+    _abi.check(lib.idx_paged_mqa_logits(
+        ctypes.byref(cache), _ptr(q), _ptr(q_scale), _ptr(w), _ptr(context_lens), int(ctx_per_row),
+        _ptr(block_table), block_table.stride(0), block_table.shape[1], B, next_n, H, _ptr(logits),
+        logits.stride(0), width, _ptr(row_end_out), _ptr(workspace), ws_bytes, _stream()))
     return logits, row_end_out
+
+
+def _paged_outputs(q, rows, width, logits, row_end_out):
+    if logits is None:
+        logits = torch.empty((rows, (width + 3) // 4 * 4), dtype=torch.float32, device=q.device)[:, :width]
+    if row_end_out is None:
+        row_end_out = torch.empty(rows, dtype=torch.int32, device=q.device)
+    return logits, row_end_out
+
+
+def _paged_workspace(lib, cache, B, next_n, H, device, workspace):
+    need = lib.idx_paged_mqa_logits_workspace(B, next_n, H, ctypes.byref(cache))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, 0 if workspace is None else workspace.numel() * workspace.element_size()
 
 
 def idx_paged_mqa_logits_block_max(pool: torch.Tensor, fmt: int, page_size: int, q: torch.Tensor,
@@ -130,10 +151,7 @@ def idx_paged_mqa_logits_block_max(pool: torch.Tensor, fmt: int, page_size: int,
     cache = _paged_inputs(pool, fmt, page_size, q, q_scale, w, context_lens, block_table)
     B, next_n, H = q.shape[:3]
     rows = B * next_n
-    if logits is None:
-        logits = torch.empty((rows, (width + 3) // 4 * 4), dtype=torch.float32, device=q.device)[:, :width]
-    if row_end_out is None:
-        row_end_out = torch.empty(rows, dtype=torch.int32, device=q.device)
+    logits, row_end_out = _paged_outputs(q, rows, width, logits, row_end_out)
     if block_size and block_max is None:
         block_max = torch.empty((rows, -(-width // block_size)), dtype=torch.float32, device=q.device)
     if block_max is not None:
@@ -141,10 +159,7 @@ def idx_paged_mqa_logits_block_max(pool: torch.Tensor, fmt: int, page_size: int,
         if block_max.stride(1) != 1:
             raise ValueError("block_max rows must be dense")
     lib = _abi.lib()
-    need = lib.idx_paged_mqa_logits_workspace(B, next_n, H, ctypes.byref(cache))
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _paged_workspace(lib, cache, B, next_n, H, q.device, workspace)
     _abi.check(lib.idx_paged_mqa_logits_block_max(
         ctypes.byref(cache), _ptr(q), _ptr(q_scale), _ptr(w), _ptr(context_lens), int(ctx_per_row),
         _ptr(block_table), block_table.stride(0), block_table.shape[1], B, next_n, H, _ptr(logits),
