@@ -196,9 +196,10 @@ __device__ __forceinline__ void reduce_scatter_step(float (&x)[32], bool upper) 
 // +0.0. The smallest key of a non-NaN float is that of -inf (0x007FFFFF), so 0 can
 // stand for "no key".
 __device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // x + 0.0 turns -0.0 into +0.0 and leaves every other non-NaN float as it is
+  // (fp32 denormals are kept: the library builds without flushing them)
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  return u ^ (uint32_t(int32_t(u) >> 31) | 0x80000000u);
 }
 
 // number of set bits of mask below this lane

@@ -247,12 +247,20 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a, uint8_t *ws) {
       for (int e = 0; e < 4; ++e) kr4[s][e] = uint32_t(x[e]);
     }
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s)
+    for (int s = 0; s < kSteps; ++s) {
+      const int cs = cb + s * 256;
+      if (uniform(int(cs >= st0 && cs + 256 <= whi))) {
+        // every column of the step is in the row (all but a row's first and last steps)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = cb + s * 256 + 4 * lane + e;
-        kr4[s][e] = (c >= st0 && c < whi) ? order_key(__uint_as_float(kr4[s][e])) : 0u;
+        for (int e = 0; e < 4; ++e) kr4[s][e] = order_key(__uint_as_float(kr4[s][e]));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = cs + 4 * lane + e;
+          kr4[s][e] = (c >= st0 && c < whi) ? order_key(__uint_as_float(kr4[s][e])) : 0u;
+        }
       }
+    }
   };
   // fn(keys of 4 consecutive columns, first column) over the wave's segment in column
   // order, each lane holding 4 consecutive columns of a step; loads again only when the
@@ -532,17 +540,32 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a, uint8_t *ws) {
   }
 
   // ---- emission in column order -------------------------------------------------------
+  // Each walk compares against its own copy of T that the optimiser cannot see
+  // through: with one shared T the compiler keeps the counting walk's comparisons
+  // alive for the emitting walk (all 32 per lane, packed into bytes and unpacked per
+  // step), which costs several times more than comparing again. Rows with no ties to
+  // place (kr3 == 0, the usual case) take walks that never look at keys equal to T.
   {
+    const bool ties = kr3 > 0;
+    uint32_t Tc = uint32_t(uniform(int(T)));
+    asm volatile("" : "+s"(Tc));
     int gt = 0, eq = 0;
-    walk([&](const uint32_t (&key)[4], int) {
+    if (!ties) {
+      walk([&](const uint32_t (&key)[4], int) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        gt += int(key[e] > T);
-        eq += int(key[e] == T);
-      }
-    }, false);
+        for (int e = 0; e < 4; ++e) gt += int(key[e] > Tc);
+      }, false);
+    } else {
+      walk([&](const uint32_t (&key)[4], int) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          gt += int(key[e] > Tc);
+          eq += int(key[e] == Tc);
+        }
+      }, false);
+    }
     gt = wave_sum(gt);
-    eq = kr3 > 0 ? wave_sum(eq) : 0;
+    eq = ties ? wave_sum(eq) : 0;
     if (lane == 0) {
       s_wcnt[0][wave] = gt;
       s_wcnt[1][wave] = eq;
@@ -556,38 +579,59 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a, uint8_t *ws) {
     int tie_run = tie0 + eqb;  // row tie rank of the next tie met in this wave
     int pos = base + gtb + max(0, min(eqb, kr3 - tie0));
     const buffer_rsrc orsrc = make_rsrc(out, uint32_t(k) * 4u);  // slots past k are dropped
-    walk([&](const uint32_t (&key)[4], int c0) {
-      bool sel[4];
-      int neq = 0;
+    uint32_t Te = uint32_t(uniform(int(T)));
+    asm volatile("" : "+s"(Te));
+    if (!ties) {
+      walk([&](const uint32_t (&key)[4], int c0) {
+        int ns = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sel[e] = key[e] > T;
-        neq += int(key[e] == T);
-      }
-      if (kr3 > 0 && __ballot(neq != 0) != 0ull) {
-        const int incl = wave_incl_scan(neq);
-        int rk = tie_run + incl - neq;
+        for (int e = 0; e < 4; ++e) ns += int(key[e] > Te);
+        const int incl = wave_incl_scan(ns);
+        int p = pos + incl - ns;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if (key[e] == T) {
-            sel[e] = rk < kr3;
-            ++rk;
+          if (key[e] > Te) {
+            __builtin_amdgcn_raw_buffer_store_b32(uint32_t(c0 + e - st0), orsrc, uint32_t(p) * 4u, 0, 0);
+            ++p;
           }
         }
-        tie_run += __builtin_amdgcn_readlane(incl, 63);
-      }
-      const int ns = int(sel[0]) + int(sel[1]) + int(sel[2]) + int(sel[3]);
-      const int incl = wave_incl_scan(ns);
-      int p = pos + incl - ns;
+        pos += __builtin_amdgcn_readlane(incl, 63);
+      }, false);
+    } else {
+      walk([&](const uint32_t (&key)[4], int c0) {
+        // bit e: key e is selected (above T, or a tie whose row rank is below kr3)
+        uint32_t sel = 0;
+        int neq = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (sel[e]) {
-          __builtin_amdgcn_raw_buffer_store_b32(uint32_t(c0 + e - st0), orsrc, uint32_t(p) * 4u, 0, 0);
-          ++p;
+        for (int e = 0; e < 4; ++e) {
+          sel |= uint32_t(key[e] > Te) << e;
+          neq += int(key[e] == Te);
         }
-      }
-      pos += __builtin_amdgcn_readlane(incl, 63);
-    }, false);
+        if (__ballot(neq != 0) != 0ull) {
+          const int incl = wave_incl_scan(neq);
+          int rk = tie_run + incl - neq;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (key[e] == Te) {
+              sel |= uint32_t(rk < kr3) << e;
+              ++rk;
+            }
+          }
+          tie_run += __builtin_amdgcn_readlane(incl, 63);
+        }
+        const int ns = __builtin_popcount(sel);
+        const int incl = wave_incl_scan(ns);
+        int p = pos + incl - ns;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if ((sel >> e) & 1u) {
+            __builtin_amdgcn_raw_buffer_store_b32(uint32_t(c0 + e - st0), orsrc, uint32_t(p) * 4u, 0, 0);
+            ++p;
+          }
+        }
+        pos += __builtin_amdgcn_readlane(incl, 63);
+      }, false);
+    }
   }
   if (solo) return;
 
