@@ -239,16 +239,20 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a, uint8_t *ws) {
   // (the raw bits land in kr4 and are converted in place, so a pass needs no second
   // set of registers)
   auto load_pass = [&](int cb) {
+    // steps at or past the segment's end are neither loaded nor converted: the walks
+    // stop before them
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      const int c = cb + s * 256 + 4 * lane;
-      const v4i x = c < whi ? buffer_load16(rsrc, uint32_t(c) * 4u) : v4i{0, 0, 0, 0};
+      if (uniform(int(cb + s * 256 < whi))) {
+        const v4i x = buffer_load16(rsrc, uint32_t(cb + s * 256 + 4 * lane) * 4u);  // zero past the row
 #pragma unroll
-      for (int e = 0; e < 4; ++e) kr4[s][e] = uint32_t(x[e]);
+        for (int e = 0; e < 4; ++e) kr4[s][e] = uint32_t(x[e]);
+      }
     }
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       const int cs = cb + s * 256;
+      if (uniform(int(cs >= whi))) break;
       if (uniform(int(cs >= st0 && cs + 256 <= whi))) {
         // every column of the step is in the row (all but a row's first and last steps)
 #pragma unroll
