@@ -62,11 +62,14 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunk = 64;
 constexpr int kMinChunksPerWave = 2;
-// Chunks a wave holds: one being scored, the rest in flight. Three for multi-row
-// (MTP) steps, whose register count allows two waves per SIMD either way; two for
-// single rows, where a third buffer would cost a wave per SIMD.
+// Chunk buffers a wave holds in registers. fp8 chunks move to the wave's LDS tile
+// before they are scored and their buffer takes the next chunk's loads at once, so
+// both buffers stay in flight while a chunk is scored (a third buffer measured slower
+// on the MTP step: 100.5 against 98.5 us). MXFP4 chunks are scored from their
+// registers: two buffers for single rows, where a third would cost a wave per SIMD,
+// three for multi-row steps.
 template <int FMT, int NR>
-constexpr int ring_depth() { return NR == 1 ? 2 : 3; }
+constexpr int ring_depth() { return FMT == 0 || NR == 1 ? 2 : 3; }
 constexpr int kTileStride = 160;  // LDS bytes per key row of a wave's fp8 tile (128 + 32: rocprofv3 counts no
                                   // bank conflicts at 160, 1.4 M cycles per MTP step at 144)
 
@@ -153,10 +156,15 @@ __global__ __launch_bounds__(64) void pool_length_kernel(PagedArgs a) {
 
 // Three waves per SIMD where one row's registers fit a third of the register file
 // (168): one row with at most 64 heads, except the fp8 gathered walk, which would
-// spill; otherwise the compiler may use them all.
+// spill. Two where the kernel fits half of it (256): asked for one wave per SIMD, the
+// compiler put each MFMA result in accumulation registers and copied it back one
+// register per score (128 extra vector instructions per MTP chunk; MTP logits 102.0
+// -> 100.5 us with the request for two). The largest (many rows and heads) need more.
 template <int FMT, int HT, int NR, bool GATHER>
 constexpr int waves_per_simd() {
-  return NR == 1 && (HT <= 2 || (HT == 4 && !(FMT == 0 && GATHER))) ? 3 : 1;
+  return NR == 1 && (HT <= 2 || (HT == 4 && !(FMT == 0 && GATHER))) ? 3
+         : ((NR <= 2 && (HT <= 4 || NR == 1)) || HT <= 2) ? 2
+                                                          : 1;
 }
 
 // GATHER: each query row walks its own candidate pool (NR = 1, one "sequence" per
@@ -373,16 +381,20 @@ void paged_logits_kernel(PagedArgs a) {
     }
   };
 
-  auto score = [&](const Chunk<FMT> &ch, int b, int c) {
-    const int col = c * kChunk + lane;
+  // fp8: raw key rows into this wave's LDS tile; each key group's MFMA B operand is read
+  // back just before its MFMAs (lane (g, n) of group kg: bytes [16g, 16g+16) and
+  // [64+16g, 64+16g+16) of key 16 kg + n), so one operand is live at a time
+  auto stage = [&](const Chunk<FMT> &ch) {
     if constexpr (FMT == 0) {
-      // raw key rows into this wave's LDS tile; each key group's MFMA B operand is read
-      // back just before its MFMAs (lane (g, n) of group kg: bytes [16g, 16g+16) and
-      // [64+16g, 64+16g+16) of key 16 kg + n), so one operand is live at a time
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         *reinterpret_cast<v4i *>(&s_tile[wave][(8 * j + (lane >> 3)) * kTileStride + (lane & 7) * 16]) = ch.raw[j];
     }
+  };
+  // scores chunk c of sequence b; fp8 keys come from the LDS tile (staged), so of ch
+  // only the key scale and the gather position are read
+  auto score = [&](const Chunk<FMT> &ch, int b, int c) {
+    const int col = c * kChunk + lane;
     float part[NR][4];
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg) {
@@ -473,21 +485,48 @@ void paged_logits_kernel(PagedArgs a) {
         ic = 0;
       }
     };
+    if constexpr (FMT == 0) {
+      // fp8: a chunk's registers are free once it is staged in LDS, so its slot takes
+      // the loads of chunk i + kRing before chunk i is scored: kRing chunks stay in
+      // flight while a chunk is scored
 #pragma unroll
-    for (int s = 0; s < kRing - 1; ++s)
-      if (iu < u1) issue_next(ring[s], rb[s], rc[s]);
-    for (int u = u0; u < u1; u += kRing) {
+      for (int s = 0; s < kRing; ++s)
+        if (iu < u1) issue_next(ring[s], rb[s], rc[s]);
+      for (int u = u0; u < u1; u += kRing) {
 #pragma unroll
-      for (int s = 0; s < kRing; ++s) {
-        if (u + s >= u1) break;
-        const int nxt = (s + kRing - 1) % kRing;  // slot of chunk u + s + kRing - 1
-        if (iu < u1) issue_next(ring[nxt], rb[nxt], rc[nxt]);
-        fill_some(2);
-        if (rb[s] != qb) {
-          load_queries(rb[s]);
-          qb = rb[s];
+        for (int s = 0; s < kRing; ++s) {
+          if (u + s >= u1) break;
+          const int b = rb[s], c = rc[s];
+          if (b != qb) {
+            load_queries(b);
+            qb = b;
+          }
+          stage(ring[s]);
+          Chunk<FMT> kept;
+          kept.ksc = ring[s].ksc;
+          if constexpr (GATHER) kept.lpos = ring[s].lpos;
+          if (iu < u1) issue_next(ring[s], rb[s], rc[s]);
+          fill_some(2);
+          score(kept, b, c);
         }
-        score(ring[s], rb[s], rc[s]);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < kRing - 1; ++s)
+        if (iu < u1) issue_next(ring[s], rb[s], rc[s]);
+      for (int u = u0; u < u1; u += kRing) {
+#pragma unroll
+        for (int s = 0; s < kRing; ++s) {
+          if (u + s >= u1) break;
+          const int nxt = (s + kRing - 1) % kRing;  // slot of chunk u + s + kRing - 1
+          if (iu < u1) issue_next(ring[nxt], rb[nxt], rc[nxt]);
+          fill_some(2);
+          if (rb[s] != qb) {
+            load_queries(rb[s]);
+            qb = rb[s];
+          }
+          score(ring[s], rb[s], rc[s]);
+        }
       }
     }
   };
