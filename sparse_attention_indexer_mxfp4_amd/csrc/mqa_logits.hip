@@ -226,17 +226,10 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
   };
   auto fetch = [&](Fetch &f, int c) {
     if constexpr (PAGED) {
-      auto clamp_page = [&](int pg) { return min(max(pg, 0), a.num_pages - 1); };
-      int pg[kStage / 16];
-#pragma unroll
-      for (int j = 0; j < kStage / 16; ++j) pg[j] = clamp_page(__builtin_amdgcn_readlane(pg_next, j));
+      // lane j: the page of group j (a select chain over per-group copies was turned
+      // into a private array in scratch memory, read back for every load)
+      const int pgv = min(max(pg_next, 0), a.num_pages - 1);
       load_pages(c + kStage);
-      auto page_of = [&](int grp) {
-        int p = pg[0];
-#pragma unroll
-        for (int j = 1; j < kStage / 16; ++j) p = grp == j ? pg[j] : p;
-        return p;
-      };
       auto within = [&](int pos) { return a.page_shift >= 0 ? pos & (a.page_size - 1) : pos % a.page_size; };
       // a wave's 16-byte pieces of load i all lie in one 16-key group, so one page: a
       // range-checked buffer load over that page's values, keys past the end out of range
@@ -246,14 +239,16 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
         const int key = idx >> 3, part = idx & 7;
         const int pos = c + key;
         const int grp = uniform(key >> 4);
-        const buffer_rsrc pr = make_rsrc(a.kbase + int64_t(page_of(grp)) * a.page_stride, uint32_t(a.page_size) * 128u);
+        const int page = __builtin_amdgcn_readlane(pgv, grp);
+        const buffer_rsrc pr = make_rsrc(a.kbase + int64_t(page) * a.page_stride, uint32_t(a.page_size) * 128u);
         f.kv[i] = buffer_load16(pr, pos < klim ? uint32_t(within(pos) * 128 + part * 16) : 0xFFFFFFF0u);
       }
       const int key = tid & (kStage - 1), pos = c + key;
+      const int kpage = __builtin_amdgcn_ds_bpermute((key >> 4) << 2, pgv);  // lane key/16's page
       f.ks = 0.f;
       if (pos < klim)
-        f.ks = *reinterpret_cast<const float *>(a.kbase + int64_t(page_of(key >> 4)) * a.page_stride +
-                                                a.page_size * 128 + within(pos) * 4);
+        f.ks = *reinterpret_cast<const float *>(a.kbase + int64_t(kpage) * a.page_stride + a.page_size * 128 +
+                                                within(pos) * 4);
     } else {
       const int64_t left = max(int64_t(a.N) - c, int64_t(0));
       const buffer_rsrc kr = make_rsrc(a.k + int64_t(c) * a.k_row_stride, range_bytes(left * a.k_row_stride));
