@@ -249,14 +249,24 @@ void paged_logits_kernel(PagedArgs a) {
   // The wave's share of 256-column units is written a few units at a time, each batch
   // after a chunk's K loads are issued: memory operations complete in issue order, so
   // stores issued ahead of the block-table and K loads would delay them.
-  const int fill_nu = (a.width + 255) / 256;
-  const int64_t fill_total = int64_t(S) * NR * fill_nu;
-  int64_t fill_next = v;  // next unit of this wave
+  // Unit u of the S * NR * fill_nu units is row u / fill_nu, columns from
+  // 256 * (u % fill_nu); a wave takes units v, v + V, ..., its row and unit stepped by
+  // V without a division per unit.
+  const int fill_nu = max((a.width + 255) / 256, 1);
+  const int fill_rows = a.width > 0 ? S * NR : 0;
+  const int fill_dr = V / fill_nu, fill_dc = V % fill_nu;
+  int fill_r = v / fill_nu, fill_c = v % fill_nu;  // this wave's next unit
   auto fill_some = [&](int units) {
-    for (int i = 0; i < units && fill_next < fill_total; ++i, fill_next += V) {
-      const int64_t r = fill_next / fill_nu;
-      const int col = int(fill_next % fill_nu) * 256 + lane * 4;
-      const int bb = int(r / NR);
+    for (int i = 0; i < units && fill_r < fill_rows; ++i) {
+      const int r = fill_r;
+      const int col = fill_c * 256 + lane * 4;
+      fill_c += fill_dc;
+      fill_r += fill_dr;
+      if (fill_c >= fill_nu) {
+        fill_c -= fill_nu;
+        ++fill_r;
+      }
+      const int bb = r / NR;
       const int tail = (s_pref[bb + 1] - s_pref[bb]) * kChunk;
       if (col >= tail && col < a.width) {
         float *p = a.logits + r * a.logits_row_stride + col;
