@@ -356,7 +356,9 @@ void paged_logits_kernel(PagedArgs a) {
   float wv[NR][HT][4];
   int qs[NR][HT];
   int end[NR];
-  auto load_queries = [&](int b) {
+  // inlined by force: a call would need the kernel arguments it captures in scratch
+  // memory (the compiler outlined it in the largest instantiations)
+  auto load_queries = [&](int b) __attribute__((always_inline)) {
     if constexpr (GATHER)
       end[0] = s_end[b];
     else

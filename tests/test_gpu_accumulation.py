@@ -104,13 +104,29 @@ def test_fp8_accumulation_bound():
                                       _dev(np.full(ROWS, KEYS, np.int32)), _dev(bt), KEYS)
     # prefill kernel (its |x| split carries the linear term on one more MFMA)
     pre = ops.idx_mqa_logits(_dev(q2), _dev(k), _dev(ones), _dev(w), _dev(ks), _dev(ke))
+    # MTP walk, two rows per sequence and 64 heads (62 of them zero): the kernel of the
+    # multi-row decode steps
+    H2, B2 = 64, ROWS // 2
+    q64 = np.zeros((ROWS, H2, D), np.uint8)
+    q64[:, :2] = q2
+    w64 = np.zeros((ROWS, H2), np.float32)
+    w64[:, :2] = w
+    lens2 = np.full(B2, KEYS, np.int32)
+    bt2 = np.tile(np.arange(KEYS // P, dtype=np.int32), (B2, 1))
+    mtp_args = (pool, "fp8", P, bt2, lens2, q64.reshape(B2, 2, H2, D), w64, B2, 2, KEYS)
+    mtp_exact = indexer.paged_logits(*mtp_args)
+    mtp_mag = indexer.paged_logits(*mtp_args, magnitude=True)
+    mtp, _ = ops.idx_paged_mqa_logits(_dev(pool), ops.FP8, P, _dev(q64.reshape(B2, 2, H2, D)), None, _dev(w64),
+                                      _dev(lens2), _dev(bt2), KEYS)
     torch.cuda.synchronize()
     r_dec = _ratio(dec.cpu().numpy().astype(np.float64), exact, mag)
     r_pre = _ratio(pre.cpu().numpy().astype(np.float64), exact, mag)
+    r_mtp = _ratio(mtp.cpu().numpy().astype(np.float64), mtp_exact, mtp_mag)
     print(f"fp8 worst |err| / sum|q k|: decode walk 2^{np.log2(max(r_dec, 1e-300)):.2f}, "
-          f"prefill 2^{np.log2(max(r_pre, 1e-300)):.2f}", flush=True)
+          f"prefill 2^{np.log2(max(r_pre, 1e-300)):.2f}, MTP walk 2^{np.log2(max(r_mtp, 1e-300)):.2f}", flush=True)
     assert r_dec <= BOUND
     assert r_pre <= BOUND
+    assert r_mtp <= BOUND
 
 
 def test_mxfp4_accumulation_bound():
