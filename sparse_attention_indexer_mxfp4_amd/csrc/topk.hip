@@ -24,6 +24,7 @@
 // counts come from extra passes over the row instead.
 #include <cstddef>
 #include <mutex>
+#include <type_traits>
 
 #include "device.h"
 #include "launch.h"
@@ -399,6 +400,12 @@ __device__ void finish_cached(Smem<NT> &sm, const uint32_t *keys, int n, int k, 
     select_digit<NT, 1024>(sm, sm.hist, kr);
     T = (p2 << 10) | uint32_t(sm.sel[0]);
     kr -= sm.sel[1];  // ties (keys equal to T) still to take, >= 1
+    if (int(sm.hist[sm.sel[0]]) == kr) {
+      // every key equal to T is taken (the usual case): the same set as keys > T - 1,
+      // and the emission then has no ties to rank
+      T -= 1u;
+      kr = 0;
+    }
     for (int i = tid; i < nc; i += NT) {
       const uint32_t c = sm.cand[i];
       const uint32_t key = (d1 << 21) | (c & 0x1FFFFFu);
@@ -415,23 +422,30 @@ __device__ void finish_cached(Smem<NT> &sm, const uint32_t *keys, int n, int k, 
   before_wave(sm, wave, lane, gt_before, eq_before);
   int pos = gt_before + min(eq_before, kr);
   int eq_run = eq_before;
-  for (int base = lo; base < hi; base += kStep * kSubSteps) {
-    uint32_t sel = 0u, eq = 0u;
+  // rows with ties to place test keys for equality; the others do not
+  auto walk = [&](auto ties) {
+    for (int base = lo; base < hi; base += kStep * kSubSteps) {
+      uint32_t sel = 0u, eq = 0u;
 #pragma unroll
-    for (int j = 0; j < kSubSteps; ++j) {
-      if (base + j * kStep < hi) {
-        const v4i kv = *reinterpret_cast<const v4i *>(keys + base + j * kStep + 4 * lane);
+      for (int j = 0; j < kSubSteps; ++j) {
+        if (base + j * kStep < hi) {
+          const v4i kv = *reinterpret_cast<const v4i *>(keys + base + j * kStep + 4 * lane);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sel |= uint32_t(uint32_t(kv[e]) > T) << (4 * j + e);
-          eq |= uint32_t(uint32_t(kv[e]) == T) << (4 * j + e);
+          for (int e = 0; e < 4; ++e) {
+            sel |= uint32_t(uint32_t(kv[e]) > T) << (4 * j + e);
+            if constexpr (decltype(ties)::value) eq |= uint32_t(uint32_t(kv[e]) == T) << (4 * j + e);
+          }
         }
       }
+      // ties in column order: the first kr of the row's ties are taken
+      if constexpr (decltype(ties)::value) sel |= take_ties<4, kSubSteps>(eq, kr, eq_run);
+      pos = emit_bits<4, kSubSteps>(sel, base, lane, pos, k, out);
     }
-    // ties in column order: the first kr of the row's ties are taken
-    if (kr > 0) sel |= take_ties<4, kSubSteps>(eq, kr, eq_run);
-    pos = emit_bits<4, kSubSteps>(sel, base, lane, pos, k, out);
-  }
+  };
+  if (kr > 0)
+    walk(std::true_type{});
+  else
+    walk(std::false_type{});
 }
 
 // Phases 3 to 5 for a row of more keys than the key cache holds but at most twice as
@@ -522,6 +536,10 @@ __device__ void finish_half(Smem<NT> &sm, uint16_t *top16, const float *lr, int 
     select_digit<NT, 1024>(sm, sm.hist, kr);
     T = (p2 << 10) | uint32_t(sm.sel[0]);
     kr -= sm.sel[1];  // ties (keys equal to T) still to take, >= 1
+    if (int(sm.hist[sm.sel[0]]) == kr) {
+      T -= 1u;  // every key equal to T is taken: keys > T - 1, no ties to rank
+      kr = 0;
+    }
     const uint32_t tp = T >> 16;
     for (int i = tid; i < nc; i += NT) {
       const uint32_t c = sm.cand[i];
@@ -544,23 +562,29 @@ __device__ void finish_half(Smem<NT> &sm, uint16_t *top16, const float *lr, int 
   before_wave(sm, wave, lane, gt_before, eq_before);
   int pos = gt_before + min(eq_before, kr);
   int eq_run = eq_before;
-  for (int base = lo; base < hi; base += kStep * kSubSteps) {
-    uint32_t sel = 0u, eq = 0u;  // bit 8 j + e: column base + kStep j + 8 lane + e
+  auto walk = [&](auto ties) {
+    for (int base = lo; base < hi; base += kStep * kSubSteps) {
+      uint32_t sel = 0u, eq = 0u;  // bit 8 j + e: column base + kStep j + 8 lane + e
 #pragma unroll
-    for (int j = 0; j < kSubSteps; ++j) {
-      if (base + j * kStep < hi) {
-        const v4i raw = *reinterpret_cast<const v4i *>(top16 + base + j * kStep + 8 * lane);
+      for (int j = 0; j < kSubSteps; ++j) {
+        if (base + j * kStep < hi) {
+          const v4i raw = *reinterpret_cast<const v4i *>(top16 + base + j * kStep + 8 * lane);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t t = (uint32_t(raw[e >> 1]) >> (16 * (e & 1))) & 0xFFFFu;
-          sel |= uint32_t(t > tp) << (8 * j + e);
-          eq |= uint32_t(t == tp) << (8 * j + e);
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t t = (uint32_t(raw[e >> 1]) >> (16 * (e & 1))) & 0xFFFFu;
+            sel |= uint32_t(t > tp) << (8 * j + e);
+            if constexpr (decltype(ties)::value) eq |= uint32_t(t == tp) << (8 * j + e);
+          }
         }
       }
+      if constexpr (decltype(ties)::value) sel |= take_ties<8, kSubSteps>(eq, kr, eq_run);
+      pos = emit_bits<8, kSubSteps>(sel, base, lane, pos, k, out);
     }
-    if (kr > 0) sel |= take_ties<8, kSubSteps>(eq, kr, eq_run);
-    pos = emit_bits<8, kSubSteps>(sel, base, lane, pos, k, out);
-  }
+  };
+  if (kr > 0)
+    walk(std::true_type{});
+  else
+    walk(std::false_type{});
 }
 
 static_assert(sizeof(Smem<1024>) + kMaxCache * sizeof(uint32_t) <= 160 * 1024, "LDS of a workgroup");

@@ -392,6 +392,10 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a, uint8_t *ws) {
         select(s_h, 1024, kr2);
         T = (p2 << 10) | uint32_t(s_sel[0]);
         kr3 = kr2 - s_sel[1];
+        if (int(s_h[s_sel[0]]) == kr3) {
+          T -= 1u;  // every key equal to T is taken: keys > T - 1, no ties to rank
+          kr3 = 0;
+        }
       }
     }
   } else if constexpr (!SOLO) {
