@@ -156,15 +156,18 @@ __global__ __launch_bounds__(64) void pool_length_kernel(PagedArgs a) {
 
 // Three waves per SIMD where one row's registers fit a third of the register file
 // (168): one row with at most 64 heads, except the fp8 gathered walk, which would
-// spill. Two where the kernel fits half of it (256): asked for one wave per SIMD, the
-// compiler put each MFMA result in accumulation registers and copied it back one
-// register per score (128 extra vector instructions per MTP chunk; MTP logits 102.0
-// -> 100.5 us with the request for two). The largest (many rows and heads) need more.
+// spill. Two where the kernel fits half of it (256), or nearly: asked for one wave per
+// SIMD, the compiler put each MFMA result in accumulation registers and copied it back
+// one register per score (128 extra vector instructions per MTP chunk; MTP logits
+// 102.0 -> 100.5 us with the request for two), and at three rows per sequence and 64
+// heads it spilled to them (next_n = 3, B = 64: fp8 90 -> 69 us, MXFP4 79 -> 54 us;
+// MXFP4 at four rows 96 -> 74 us). fp8 at four rows and 64 heads spills to scratch
+// memory at two waves (110 against 141 us) and keeps one, as do 128 heads.
 template <int FMT, int HT, int NR, bool GATHER>
 constexpr int waves_per_simd() {
   return NR == 1 && (HT <= 2 || (HT == 4 && !(FMT == 0 && GATHER))) ? 3
-         : ((NR <= 2 && (HT <= 4 || NR == 1)) || HT <= 2) ? 2
-                                                          : 1;
+         : ((NR <= 2 && (HT <= 4 || NR == 1)) || HT <= 2 || (HT == 4 && (NR == 3 || FMT == 1))) ? 2
+                                                                                              : 1;
 }
 
 // GATHER: each query row walks its own candidate pool (NR = 1, one "sequence" per
