@@ -466,6 +466,35 @@ idx_status idx_remap_compact_topk(int32_t *topk, int64_t topk_row_stride, int32_
                                   const int32_t *cand, int64_t cand_row_stride, int32_t n_cand, int32_t block_size,
                                   int32_t row_repeat, hipStream_t stream);
 
+/*
+ * Debug build. The library can be built a second time with -DIDX_DEBUG (the build
+ * script links it as libidx_debug.so next to libidx.so). Its kernels compute exactly
+ * what the release kernels compute and also record, in a device word, every
+ * device-resident value that had to be clamped or dropped, one bit per kind:
+ */
+#define IDX_DBG_LENGTH 1u   /* a sequence length or row bound outside its range: a
+                               context length < 0, or a row end past
+                               min(width, max_blocks*page_size) (the table's reach
+                               alone for the gathered walk); a row_start < 0 or a
+                               row_end < 0 or past the row's columns (idx_mqa_logits,
+                               idx_topk, idx_candidate_blocks, idx_apply_candidate_mask) */
+#define IDX_DBG_PAGE 2u     /* a block-table entry outside [0, num_pages) read for a
+                               key below its row's end */
+#define IDX_DBG_SLOT 4u     /* a slot >= 0 whose page is outside the pool (the key is
+                               dropped as padding would be) */
+#define IDX_DBG_POSITION 8u /* a rotary position outside [0, max_position) */
+#define IDX_DBG_SEQ 16u     /* a row_seq entry outside [0, B) (idx_topk_to_slots) */
+/*
+ * idx_debug_flags - waits for the current device to finish its work (like
+ * hipDeviceSynchronize), then stores the OR of the recorded bits in *flags and, when
+ * clear != 0, resets them. The bits persist across calls until cleared. The release
+ * library records nothing: *flags is always 0. Not for use under graph capture.
+ * IDX_ERR_NULL for a NULL flags; IDX_ERR_LAUNCH when a HIP call fails.
+ * idx_debug_build - 1 for the debug build, 0 for the release build.
+ */
+idx_status idx_debug_flags(uint32_t *flags, int32_t clear);
+int32_t idx_debug_build(void);
+
 /* Static text naming a status; never NULL. */
 const char *idx_status_str(idx_status s);
 /* IDX_ABI_VERSION of the built library. */

@@ -3,10 +3,12 @@ missing: there is no fallback implementation."""
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libidx.so")
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libidx_debug.so")
 
 IDX_OK = 0
 IDX_KV_FP8_E4M3 = 0
@@ -26,8 +28,11 @@ EXPORTS = (
     "idx_topk_workspace", "idx_k_store", "idx_q_quant", "idx_k_norm_rope_store", "idx_q_rope_quant",
     "idx_topk_to_slots", "idx_paged_mqa_logits_block_max", "idx_candidate_blocks", "idx_apply_candidate_mask",
     "idx_paged_mqa_logits_gather", "idx_remap_compact_topk", "idx_paged_prefill_logits", "idx_topk_noalloc",
-    "idx_status_str", "idx_abi_version",
+    "idx_debug_flags", "idx_debug_build", "idx_status_str", "idx_abi_version",
 )
+
+# idx_debug_flags bits: device-resident values the kernels had to clamp or drop
+DBG_LENGTH, DBG_PAGE, DBG_SLOT, DBG_POSITION, DBG_SEQ = 1, 2, 4, 8, 16
 
 
 class PagedCache(ctypes.Structure):
@@ -83,6 +88,8 @@ def _declare(lib: ctypes.CDLL) -> None:
                                                _I64, _I32, _I32, _I32, _P, _I64, _P, _P]),
         "idx_remap_compact_topk": (_I32, [_P, _I64, _I32, _I32, _P, _I64, _I32, _I32, _I32, _P]),
         "idx_paged_prefill_logits": (_I32, [cache_p, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _I64, _I32, _P]),
+        "idx_debug_flags": (_I32, [ctypes.POINTER(ctypes.c_uint32), _I32]),
+        "idx_debug_build": (_I32, []),
         "idx_status_str": (ctypes.c_char_p, [_I32]),
         "idx_abi_version": (_I32, []),
     }
@@ -92,19 +99,45 @@ def _declare(lib: ctypes.CDLL) -> None:
         fn.argtypes = args
 
 
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m sparse_attention_indexer_mxfp4_amd.build`")
+    handle = ctypes.CDLL(path)
+    _declare(handle)
+    if handle.idx_abi_version() != ABI_VERSION:
+        raise ImportError(f"{os.path.basename(path)} ABI {handle.idx_abi_version()} != {ABI_VERSION}")
+    return handle
+
+
 def lib() -> ctypes.CDLL:
     """The loaded library (loaded once). Raises if libidx.so has not been built."""
-    global _lib
+    global _lib, _release
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(
-                f"{LIB_PATH} is missing: build it with `python -m sparse_attention_indexer_mxfp4_amd.build`")
-        handle = ctypes.CDLL(LIB_PATH)
-        _declare(handle)
-        if handle.idx_abi_version() != ABI_VERSION:
-            raise ImportError(f"libidx ABI {handle.idx_abi_version()} != {ABI_VERSION}")
-        _lib = handle
+        _release = _load(LIB_PATH)
+        _lib = _release
     return _lib
+
+
+_release = None
+_debug = None
+
+
+@contextlib.contextmanager
+def debug_build():
+    """Within the block, every call goes to libidx_debug.so (the -DIDX_DEBUG build),
+    which yields the same results and records clamped device-resident values for
+    idx_debug_flags. Not thread-safe: the switch is process-wide."""
+    global _lib, _debug
+    if _debug is None:
+        _debug = _load(DEBUG_LIB_PATH)
+        if _debug.idx_debug_build() != 1:
+            raise ImportError(f"{DEBUG_LIB_PATH} is not a debug build")
+    lib()
+    _lib = _debug
+    try:
+        yield _debug
+    finally:
+        _lib = _release
 
 
 def check(status: int) -> None:

@@ -1,5 +1,7 @@
-"""Build libidx.so (the indexer's C ABI and its gfx950 HIP kernels) and libidx_calib.so
-(the measurement kernels of include/idx_calib.h) in-tree with hipcc.
+"""Build libidx.so (the indexer's C ABI and its gfx950 HIP kernels), libidx_debug.so
+(the same sources with -DIDX_DEBUG: every clamped device-resident value is recorded
+for idx_debug_flags) and libidx_calib.so (the measurement kernels of
+include/idx_calib.h) in-tree with hipcc.
 
 Every HIP source compiles for gfx950 only, with packed-fp32 instruction selection
 disabled (``-Xclang -target-feature -Xclang -packed-fp32-ops``; hipcc's host pass
@@ -21,6 +23,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libidx.so")
+DEBUG_LIB = os.path.join(PKG, "libidx_debug.so")
 CALIB_SRC = os.path.join(CSRC, "calib", "calib.hip")
 CALIB_LIB = os.path.join(PKG, "libidx_calib.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -35,8 +38,8 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str, extra: list[str]) -> tuple[str, str]:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, extra: list[str], out_dir: str = BUILD) -> tuple[str, str]:
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
     cmd = [HIPCC, *COMMON, *extra]
     if src.endswith(".hip"):
         cmd += DEVICE + ["-x", "hip"]
@@ -57,21 +60,25 @@ def _link(objs: list[str], lib: str) -> None:
 
 
 def build(verbose: bool = False, extra: list[str] | None = None, jobs: int = 8) -> str:
-    """Compile every source and link libidx.so and libidx_calib.so; returns libidx.so's
-    path. Always rebuilds."""
-    os.makedirs(BUILD, exist_ok=True)
+    """Compile every source and link libidx.so, libidx_debug.so and libidx_calib.so;
+    returns libidx.so's path. Always rebuilds."""
+    debug_dir = os.path.join(BUILD, "debug")
+    os.makedirs(debug_dir, exist_ok=True)
     extra = list(extra or [])
-    srcs = sources() + [CALIB_SRC]
+    release = sources() + [CALIB_SRC]
+    jobs_list = [(s, extra, BUILD) for s in release] + [(s, extra + ["-DIDX_DEBUG"], debug_dir) for s in sources()]
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(lambda s: _compile(s, extra), srcs))
+        results = list(ex.map(lambda j: _compile(*j), jobs_list))
     if verbose:
         for obj, err in results:
             noise = [ln for ln in err.splitlines() if "packed-fp32-ops" not in ln]
             if noise:
                 print(obj, "\n".join(noise), file=sys.stderr)
     objs = [o for o, _ in results]
-    _link(objs[:-1], LIB)
-    _link(objs[-1:], CALIB_LIB)
+    n = len(release)
+    _link(objs[:n - 1], LIB)
+    _link(objs[n - 1:n], CALIB_LIB)
+    _link(objs[n:], DEBUG_LIB)
     return LIB
 
 

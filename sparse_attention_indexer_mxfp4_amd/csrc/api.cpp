@@ -390,6 +390,34 @@ idx_status idx_topk_to_slots(const int32_t *topk, int64_t topk_row_stride, int32
   return launched(idx::launch_topk_to_slots(a, stream));
 }
 
+idx_status idx_debug_flags(uint32_t *flags, int32_t clear) {
+  if (!flags) return IDX_ERR_NULL;
+  *flags = 0;
+#ifdef IDX_DEBUG
+  if (hipDeviceSynchronize() != hipSuccess) return IDX_ERR_LAUNCH;
+  hipError_t (*const words[])(uint32_t *, bool) = {
+      idx::debug_word_mqa_logits, idx::debug_word_paged_logits, idx::debug_word_paged_prefill,
+      idx::debug_word_topk,       idx::debug_word_topk_coop,    idx::debug_word_candidates,
+      idx::debug_word_quant,      idx::debug_word_slots};
+  for (auto word : words) {
+    uint32_t v = 0;
+    if (word(&v, clear != 0) != hipSuccess) return IDX_ERR_LAUNCH;
+    *flags |= v;
+  }
+#else
+  (void)clear;
+#endif
+  return IDX_OK;
+}
+
+int32_t idx_debug_build(void) {
+#ifdef IDX_DEBUG
+  return 1;
+#else
+  return 0;
+#endif
+}
+
 const char *idx_status_str(idx_status s) {
   switch (s) {
     case IDX_OK: return "IDX_OK";

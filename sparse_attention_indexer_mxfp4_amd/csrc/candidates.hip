@@ -10,6 +10,7 @@
 // Both are a few bytes per column or entry: the mask only writes (-inf over the
 // non-candidate part of [0, end), from a per-row block bitmap in LDS), the remap reads
 // one candidate entry per top-k entry.
+#include "debug.h"
 #include "device.h"
 #include "launch.h"
 
@@ -23,6 +24,7 @@ __global__ __launch_bounds__(kMaskThreads) void candidate_mask_kernel(MaskArgs a
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int end = min(max(a.row_end[r], 0), a.width);
+  IDX_DEBUG_NOTE(a.row_end[r] < 0 || a.row_end[r] > a.width, IDX_DBG_LENGTH);
   const int bsh = 31 - __builtin_clz(a.block_size);
   const int nb = (end >> bsh) + ((end & (a.block_size - 1)) != 0);
   for (int i = tid; i < nb; i += kMaskThreads) s_flag[i] = 0;
@@ -78,5 +80,7 @@ hipError_t launch_remap_compact_topk(const RemapArgs &a, hipStream_t stream) {
   remap_kernel<<<dim3(unsigned((n + 255) / 256)), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
+
+IDX_DEBUG_READER(debug_word_candidates)
 
 }  // namespace idx

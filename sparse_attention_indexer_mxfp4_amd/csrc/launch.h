@@ -183,4 +183,17 @@ hipError_t launch_topk_to_slots(const SlotsArgs &a, hipStream_t stream);
 hipError_t launch_candidate_mask(const MaskArgs &a, hipStream_t stream);
 hipError_t launch_remap_compact_topk(const RemapArgs &a, hipStream_t stream);
 
+#ifdef IDX_DEBUG
+// The debug build's device word of each kernel source (current device): copied to
+// *out, reset with `clear`.
+hipError_t debug_word_mqa_logits(uint32_t *out, bool clear);
+hipError_t debug_word_paged_logits(uint32_t *out, bool clear);
+hipError_t debug_word_paged_prefill(uint32_t *out, bool clear);
+hipError_t debug_word_topk(uint32_t *out, bool clear);
+hipError_t debug_word_topk_coop(uint32_t *out, bool clear);
+hipError_t debug_word_candidates(uint32_t *out, bool clear);
+hipError_t debug_word_quant(uint32_t *out, bool clear);
+hipError_t debug_word_slots(uint32_t *out, bool clear);
+#endif
+
 }  // namespace idx

@@ -39,6 +39,7 @@
 // the same LDS staging and epilogue.
 #include <climits>
 
+#include "debug.h"
 #include "device.h"
 #include "launch.h"
 
@@ -110,6 +111,7 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
     active[rr] = r < a.M;
     rlo[rr] = active[rr] && a.row_start ? a.row_start[r] : 0;
     rhi[rr] = active[rr] ? min(a.row_end[r], klim) : 0;
+    IDX_DEBUG_NOTE(active[rr] && (rlo[rr] < 0 || a.row_end[r] < 0 || a.row_end[r] > klim), IDX_DBG_LENGTH);
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       const int h = ht * 16 + n;
@@ -229,6 +231,7 @@ __global__ __launch_bounds__(256, 2) void mqa_logits_fp8_kernel(MqaArgs a, int s
       // lane j: the page of group j (a select chain over per-group copies was turned
       // into a private array in scratch memory, read back for every load)
       const int pgv = min(max(pg_next, 0), a.num_pages - 1);
+      IDX_DEBUG_NOTE(c + 16 * (lane & (kStage / 16 - 1)) < hi && pgv != pg_next, IDX_DBG_PAGE);
       load_pages(c + kStage);
       auto within = [&](int pos) { return a.page_shift >= 0 ? pos & (a.page_size - 1) : pos % a.page_size; };
       // a wave's 16-byte pieces of load i all lie in one 16-key group, so one page: a
@@ -396,5 +399,7 @@ hipError_t launch_mqa_logits(const MqaArgs &a, int num_cus, hipStream_t stream) 
   }
   return hipGetLastError();
 }
+
+IDX_DEBUG_READER(debug_word_mqa_logits)
 
 }  // namespace idx

@@ -53,6 +53,7 @@
 #include <climits>
 #include <mutex>
 
+#include "debug.h"
 #include "device.h"
 #include "launch.h"
 
@@ -89,6 +90,7 @@ __device__ __forceinline__ void row_ends(const PagedArgs &a, int b, int cap, int
   for (int j = 0; j < NR; ++j) {
     const int e = a.ctx_per_row ? a.context_lens[b * NR + j] : a.context_lens[b] - NR + j + 1;
     end[j] = min(max(e, 0), cap);
+    IDX_DEBUG_NOTE((a.ctx_per_row ? e : a.context_lens[b]) < 0 || e > cap, IDX_DBG_LENGTH);
   }
 }
 
@@ -119,6 +121,7 @@ struct Chunk<1> {
 __device__ __forceinline__ int gather_row_end(const PagedArgs &a, int r, int cap) {
   const int nn = a.next_n;
   const int e = a.ctx_per_row ? a.context_lens[r] : a.context_lens[r / nn] - nn + r % nn + 1;
+  IDX_DEBUG_NOTE((a.ctx_per_row ? e : a.context_lens[r / nn]) < 0 || e > cap, IDX_DBG_LENGTH);
   return min(max(e, 0), cap);
 }
 
@@ -303,11 +306,13 @@ void paged_logits_kernel(PagedArgs a) {
               pos = p;
               const int pi = a.page_shift >= 0 ? p >> a.page_shift : p / P;
               pg = min(max(a.block_table[int64_t(bb / a.next_n) * a.block_table_stride + pi], 0), a.num_pages - 1);
+              IDX_DEBUG_NOTE(a.block_table[int64_t(bb / a.next_n) * a.block_table_stride + pi] != pg, IDX_DBG_PAGE);
             }
           }
         } else {
           const int pi = a.page_shift >= 0 ? s >> a.page_shift : s / P;
           pg = min(max(a.block_table[int64_t(bb) * a.block_table_stride + pi], 0), a.num_pages - 1);
+          IDX_DEBUG_NOTE(a.block_table[int64_t(bb) * a.block_table_stride + pi] != pg, IDX_DBG_PAGE);
         }
       }
     }
@@ -616,5 +621,7 @@ hipError_t launch_paged_logits(const PagedArgs &a, int num_cus, hipStream_t stre
   const size_t lds = a.cand ? size_t(3 * a.B * a.next_n + 1) * sizeof(int) : size_t(2 * a.B + 1) * sizeof(int);
   return a.fmt == 0 ? launch_fmt<0>(a, num_cus, lds, stream) : launch_fmt<1>(a, num_cus, lds, stream);
 }
+
+IDX_DEBUG_READER(debug_word_paged_logits)
 
 }  // namespace idx

@@ -31,6 +31,7 @@
 // the most keys).
 #include <climits>
 
+#include "debug.h"
 #include "device.h"
 #include "launch.h"
 
@@ -73,6 +74,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_fp4_kernel(PagedArgs a, 
   if (tid < 64) {
     int hi = 0;
     if (lane < kRowsPerWG && row0 + lane < M) hi = min(max(a.context_lens[row0 + lane], 0), cap);
+    IDX_DEBUG_NOTE(lane < kRowsPerWG && row0 + lane < M && hi != a.context_lens[row0 + lane], IDX_DBG_LENGTH);
     for (int off = 4; off > 0; off >>= 1) hi = max(hi, __shfl_xor(hi, off));
     if (lane == 0) s_hi = hi;
   }
@@ -200,6 +202,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_fp4_kernel(PagedArgs a, 
       const int pi = a.page_shift >= 0 ? pos >> a.page_shift : pos / P;
       const int e0 = a.page_shift >= 0 ? pos & (P - 1) : pos % P;
       const int page = min(max(a.block_table[pi], 0), a.num_pages - 1);
+      IDX_DEBUG_NOTE(a.block_table[pi] != page, IDX_DBG_PAGE);
       const uint8_t *pb = a.base + int64_t(page) * a.page_stride;
       const int run = e0 >> 4;
       f.kv = load16(pb + run * 1024 + lane * 16);
@@ -310,5 +313,7 @@ hipError_t launch_paged_prefill_fp4(const PagedArgs &a, int num_cus, hipStream_t
     paged_prefill_fp4_kernel<4><<<grid, 256, 0, stream>>>(a, split_keys);
   return hipGetLastError();
 }
+
+IDX_DEBUG_READER(debug_word_paged_prefill)
 
 }  // namespace idx

@@ -22,6 +22,7 @@
 //           layout: packed byte j of entry e at run*1024 + (j/16)*256 + (e%16)*16 + j%16,
 //           scale i at P*64 + run*64 + i*16 + e%16 (run = e/16); the query goes to
 //           [T, H, 64] bytes plus one int32 per head, byte i for block i.
+#include "debug.h"
 #include "device.h"
 #include "launch.h"
 
@@ -139,6 +140,7 @@ __device__ __forceinline__ void rope8(float (&x)[8], const float *cos_sin, int64
 }
 
 __device__ __forceinline__ int64_t clamp_pos(int64_t p, int max_position) {
+  IDX_DEBUG_NOTE(p < 0 || p >= max_position, IDX_DBG_POSITION);
   return p < 0 ? 0 : (p >= max_position ? int64_t(max_position - 1) : p);
 }
 
@@ -188,6 +190,7 @@ __global__ __launch_bounds__(256) void k_store_kernel(KStoreArgs a) {
   bool valid = i < a.N;
   const int64_t slot = valid ? a.slots[i] : -1;
   const int64_t page = slot >= 0 ? slot / a.page_size : -1;
+  IDX_DEBUG_NOTE(slot >= 0 && page >= a.num_pages, IDX_DBG_SLOT);
   valid = valid && slot >= 0 && page < a.num_pages;  // outside the pool: skipped like padding
   float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (valid) load_row8(a.k, a.k_dtype, int64_t(i) * a.k_row_stride + 8 * l, rows_vec(a.k, a.k_dtype, a.k_row_stride), x);
@@ -284,5 +287,7 @@ hipError_t launch_q_quant(const QQuantArgs &a, hipStream_t stream) {
   q_quant_kernel<<<dim3(unsigned(grid)), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
+
+IDX_DEBUG_READER(debug_word_quant)
 
 }  // namespace idx

@@ -8,6 +8,7 @@
 // running scan of the counts into indptr, and the per-row ordered write, where each
 // wave places its 64 entries with a ballot and the waves of a step take consecutive
 // ranges through a scan of their counts.
+#include "debug.h"
 #include "device.h"
 #include "launch.h"
 
@@ -22,6 +23,7 @@ __device__ __forceinline__ int lane_prefix(uint64_t mask) {
 
 __device__ __forceinline__ int row_seq(const SlotsArgs &a, int r) {
   const int b = a.row_seq ? a.row_seq[r] : r / a.next_n;
+  IDX_DEBUG_NOTE(b < 0 || b >= a.B, IDX_DBG_SEQ);
   return min(max(b, 0), a.B - 1);
 }
 
@@ -123,5 +125,7 @@ hipError_t launch_topk_to_slots(const SlotsArgs &a, hipStream_t stream) {
   if (a.rows > 0) write_kernel<<<dim3(a.rows), kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
+
+IDX_DEBUG_READER(debug_word_slots)
 
 }  // namespace idx

@@ -26,6 +26,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "debug.h"
 #include "device.h"
 #include "launch.h"
 
@@ -599,6 +600,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int cache_cap) {
   const int start = a.row_start ? min(max(a.row_start[row], 0), a.width) : 0;
   const int e_in = max(a.row_end[row], 0);
   const int end = min(a.end_div == 1 ? e_in : e_in / a.end_div + (e_in % a.end_div != 0), a.width);
+  IDX_DEBUG_NOTE((a.row_start && (a.row_start[row] < 0 || a.row_start[row] > a.width)) || a.row_end[row] < 0 ||
+                 (a.end_div == 1 ? e_in : e_in / a.end_div + (e_in % a.end_div != 0)) > a.width,
+             IDX_DBG_LENGTH);
   const int n = max(end - start, 0);
   const int k = a.k;
   int32_t *out = a.out + int64_t(row) * a.out_row_stride;
@@ -779,5 +783,7 @@ hipError_t launch_topk(const TopkArgs &a, int num_cus, void *scratch, size_t scr
     topk_kernel<1024><<<dim3(a.rows), 1024, lds, stream>>>(a, cap);
   return hipGetLastError();
 }
+
+IDX_DEBUG_READER(debug_word_topk)
 
 }  // namespace idx

@@ -50,6 +50,7 @@
 #include <climits>
 #include <mutex>
 
+#include "debug.h"
 #include "device.h"
 #include "launch.h"
 
@@ -180,6 +181,9 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a, uint8_t *ws) {
     st0 = a.row_start ? min(max(a.row_start[row], 0), a.width) : 0;
     const int e_in = max(a.row_end[row], 0);
     const int en0 = min(a.end_div == 1 ? e_in : e_in / a.end_div + (e_in % a.end_div != 0), a.width);
+    IDX_DEBUG_NOTE((a.row_start && (a.row_start[row] < 0 || a.row_start[row] > a.width)) || a.row_end[row] < 0 ||
+                   (a.end_div == 1 ? e_in : e_in / a.end_div + (e_in % a.end_div != 0)) > a.width,
+               IDX_DBG_LENGTH);
     en = max(en0, st0);
   };
   int r, g0 = 0, u = 0, nu = 1, seg = 0, st0, en;
@@ -718,5 +722,7 @@ hipError_t launch_topk_solo(const TopkArgs &a, hipStream_t stream) {
   topk_reg_kernel<256, 32, true><<<dim3(a.rows), 256, 0, stream>>>(a, nullptr);
   return hipGetLastError();
 }
+
+IDX_DEBUG_READER(debug_word_topk_coop)
 
 }  // namespace idx

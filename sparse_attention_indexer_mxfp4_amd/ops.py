@@ -406,3 +406,14 @@ def idx_topk_to_slots(topk: torch.Tensor, block_table: torch.Tensor, page_size: 
                                             _ptr(indptr), _ptr(lens), _stream()))
     return slots, indptr, lens[:rows]
 
+
+
+debug_build = _abi.debug_build  # `with ops.debug_build():` routes the calls to libidx_debug.so
+
+
+def idx_debug_flags(clear: bool = True) -> int:
+    """The IDX_DBG_* bits (_abi.DBG_*) the debug build has recorded on the current device
+    since they were last cleared; always 0 for the release build. Waits for the device."""
+    out = ctypes.c_uint32(0)
+    _abi.check(_abi.lib().idx_debug_flags(ctypes.byref(out), int(clear)))
+    return int(out.value)
