@@ -59,14 +59,16 @@ def _link(objs: list[str], lib: str) -> None:
     os.replace(tmp, lib)
 
 
-def build(verbose: bool = False, extra: list[str] | None = None, jobs: int = 8) -> str:
-    """Compile every source and link libidx.so, libidx_debug.so and libidx_calib.so;
-    returns libidx.so's path. Always rebuilds."""
+def build(verbose: bool = False, extra: list[str] | None = None, jobs: int = 8, debug: bool = True) -> str:
+    """Compile every source and link libidx.so, libidx_debug.so (unless debug is False)
+    and libidx_calib.so; returns libidx.so's path. Always rebuilds."""
     debug_dir = os.path.join(BUILD, "debug")
     os.makedirs(debug_dir, exist_ok=True)
     extra = list(extra or [])
     release = sources() + [CALIB_SRC]
-    jobs_list = [(s, extra, BUILD) for s in release] + [(s, extra + ["-DIDX_DEBUG"], debug_dir) for s in sources()]
+    jobs_list = [(s, extra, BUILD) for s in release]
+    if debug:
+        jobs_list += [(s, extra + ["-DIDX_DEBUG"], debug_dir) for s in sources()]
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         results = list(ex.map(lambda j: _compile(*j), jobs_list))
     if verbose:
@@ -78,7 +80,8 @@ def build(verbose: bool = False, extra: list[str] | None = None, jobs: int = 8) 
     n = len(release)
     _link(objs[:n - 1], LIB)
     _link(objs[n - 1:n], CALIB_LIB)
-    _link(objs[n:], DEBUG_LIB)
+    if debug:
+        _link(objs[n:], DEBUG_LIB)
     return LIB
 
 
