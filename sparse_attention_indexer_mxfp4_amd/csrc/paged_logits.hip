@@ -21,11 +21,14 @@
 //   - holds its sequence's queries as MFMA A operands (16 heads x 128 channels per
 //     tile), reloading them when its share crosses into the next sequence.
 // K bytes go straight into MFMA B operands:
-//   fp8   lane L loads 16 bytes of key 8j + L/8 at byte 16 (L%8) for j = 0..7, so a
-//         wavefront load covers 8 whole key rows of the block-flat page; the wave
-//         stages them in its own LDS tile and reads back the MFMA B operands (lane L:
-//         key L%16 of the group, bytes [16g, 16g+16) and [64+16g, 64+16g+16),
-//         g = L/16, the query using the same byte order);
+//   fp8   lane L loads bytes [16g, 16g+16) and [64+16g, 64+16g+16) of key L%16 of
+//         each 16-key group, g = L/16 (the query uses the same byte order): the MFMA
+//         B operand itself. A wavefront load reads 64 of the 128 bytes of 16
+//         consecutive key rows; its partner load reads the other halves right after.
+//         (Whole key rows per load, passed through an LDS tile to form the operands,
+//         measured slower on an MI355X: MTP logits 99.6 against 96.4 us, B = 32
+//         decode 15.3 against 15.0 us; only the fp8 gathered walk lost, 31.5 against
+//         32.2 us);
 //   MXFP4 lane L loads 16 bytes at run base + 16L - the run stores [chunk, key,
 //         byte], so one wavefront load covers the run's kilobyte exactly and lands
 //         in the scaled MFMA's operand order - plus the e8m0 byte at
@@ -63,16 +66,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunk = 64;
 constexpr int kMinChunksPerWave = 2;
-// Chunk buffers a wave holds in registers. fp8 chunks move to the wave's LDS tile
-// before they are scored and their buffer takes the next chunk's loads at once, so
-// both buffers stay in flight while a chunk is scored (a third buffer measured slower
-// on the MTP step: 100.5 against 98.5 us). MXFP4 chunks are scored from their
-// registers: two buffers for single rows, where a third would cost a wave per SIMD,
-// three for multi-row steps.
+// Chunk buffers a wave holds in registers; a chunk is scored from its buffer while
+// the others are in flight. Two buffers for single rows, where a third would cost a
+// wave per SIMD, and for fp8 (a third measured slower on the MTP step: 98.5 against
+// 96.4 us); three for multi-row MXFP4 steps.
 template <int FMT, int NR>
 constexpr int ring_depth() { return FMT == 0 || NR == 1 ? 2 : 3; }
-constexpr int kTileStride = 160;  // LDS bytes per key row of a wave's fp8 tile (128 + 32: rocprofv3 counts no
-                                  // bank conflicts at 160, 1.4 M cycles per MTP step at 144)
 
 // largest b in [0, B) with pref[b] <= u (pref[B] > u)
 __device__ __forceinline__ int find_seq(const int *pref, int B, int u) {
@@ -94,10 +93,8 @@ __device__ __forceinline__ void row_ends(const PagedArgs &a, int b, int cap, int
   }
 }
 
-// One 64-key chunk in registers. fp8: raw[j] holds bytes [16 (l % 8), +16) of key
-// 8 j + l / 8 (lane l): whole 128-byte key rows, so each wavefront load reads one
-// kilobyte of consecutive memory; the MFMA operands are formed through this wave's
-// LDS tile at scoring time. MXFP4: kb[kg] is already the B operand of key group kg.
+// One 64-key chunk in registers: the MFMA B operand of each 16-key group kg, for fp8
+// the two halves raw[2 kg] and raw[2 kg + 1], for MXFP4 kb[kg].
 template <int FMT>
 struct Chunk;
 // The gather walk also keeps, in lane L, the position of the first key of L's own
@@ -158,8 +155,8 @@ __global__ __launch_bounds__(64) void pool_length_kernel(PagedArgs a) {
 }
 
 // Three waves per SIMD where one row's registers fit a third of the register file
-// (168): one row with at most 64 heads, except the fp8 gathered walk, which would
-// spill. Two where the kernel fits half of it (256), or nearly: asked for one wave per
+// (168): one row with at most 64 heads, except the fp8 gathered walk (it fits, at 162
+// registers, but ran no faster: 32.2 us either way). Two where the kernel fits half of it (256), or nearly: asked for one wave per
 // SIMD, the compiler put each MFMA result in accumulation registers and copied it back
 // one register per score (128 extra vector instructions per MTP chunk; MTP logits
 // 102.0 -> 100.5 us with the request for two), and at three rows per sequence and 64
@@ -180,7 +177,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
 void paged_logits_kernel(PagedArgs a) {
   extern __shared__ int s_lds[];  // pref[S + 1], len[S] (+ end[S] for the gather walk)
   __shared__ int s_scan[kThreads / 64];
-  __shared__ __attribute__((aligned(16))) uint8_t s_tile[FMT == 0 ? kThreads / 64 : 1][FMT == 0 ? kChunk * kTileStride : 16];
   const int S = GATHER ? a.B * a.next_n : a.B;  // walks: sequences, or rows for the gather walk
   int *s_pref = s_lds;
   int *s_len = s_lds + S + 1;
@@ -346,9 +342,9 @@ void paged_logits_kernel(PagedArgs a) {
         const uint8_t *pb = a.base + int64_t(page) * a.page_stride;
         const int e0 = a.page_shift >= 0 ? kpos & (P - 1) : kpos % P;
         if constexpr (FMT == 0) {
-          const uint8_t *p = pb + (e0 + (lane >> 3)) * 128 + (lane & 7) * 16;
+          const uint8_t *p = pb + (e0 + n) * 128 + g * 16;
           ch.raw[2 * kg] = load16(p);
-          ch.raw[2 * kg + 1] = load16(p + 8 * 128);
+          ch.raw[2 * kg + 1] = load16(p + 64);
           if (g == kg) ch.ksc = *reinterpret_cast<const float *>(pb + P * 128 + 4 * (e0 + n));
         } else {
           const int run_i = e0 >> 4;
@@ -401,18 +397,7 @@ void paged_logits_kernel(PagedArgs a) {
     }
   };
 
-  // fp8: raw key rows into this wave's LDS tile; each key group's MFMA B operand is read
-  // back just before its MFMAs (lane (g, n) of group kg: bytes [16g, 16g+16) and
-  // [64+16g, 64+16g+16) of key 16 kg + n), so one operand is live at a time
-  auto stage = [&](const Chunk<FMT> &ch) {
-    if constexpr (FMT == 0) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<v4i *>(&s_tile[wave][(8 * j + (lane >> 3)) * kTileStride + (lane & 7) * 16]) = ch.raw[j];
-    }
-  };
-  // scores chunk c of sequence b; fp8 keys come from the LDS tile (staged), so of ch
-  // only the key scale and the gather position are read
+  // scores chunk c of sequence b
   auto score = [&](const Chunk<FMT> &ch, int b, int c) {
     const int col = c * kChunk + lane;
     float part[NR][4];
@@ -420,8 +405,7 @@ void paged_logits_kernel(PagedArgs a) {
     for (int kg = 0; kg < 4; ++kg) {
       v8i kb;
       if constexpr (FMT == 0) {
-        const uint8_t *t = &s_tile[wave][(kg * 16 + n) * kTileStride + g * 16];
-        kb = cat(*reinterpret_cast<const v4i *>(t), *reinterpret_cast<const v4i *>(t + 64));
+        kb = cat(ch.raw[2 * kg], ch.raw[2 * kg + 1]);
       } else {
         kb = ch.kb[kg];
       }
@@ -505,48 +489,21 @@ void paged_logits_kernel(PagedArgs a) {
         ic = 0;
       }
     };
-    if constexpr (FMT == 0) {
-      // fp8: a chunk's registers are free once it is staged in LDS, so its slot takes
-      // the loads of chunk i + kRing before chunk i is scored: kRing chunks stay in
-      // flight while a chunk is scored
 #pragma unroll
-      for (int s = 0; s < kRing; ++s)
-        if (iu < u1) issue_next(ring[s], rb[s], rc[s]);
-      for (int u = u0; u < u1; u += kRing) {
+    for (int s = 0; s < kRing - 1; ++s)
+      if (iu < u1) issue_next(ring[s], rb[s], rc[s]);
+    for (int u = u0; u < u1; u += kRing) {
 #pragma unroll
-        for (int s = 0; s < kRing; ++s) {
-          if (u + s >= u1) break;
-          const int b = rb[s], c = rc[s];
-          if (b != qb) {
-            load_queries(b);
-            qb = b;
-          }
-          stage(ring[s]);
-          Chunk<FMT> kept;
-          kept.ksc = ring[s].ksc;
-          if constexpr (GATHER) kept.lpos = ring[s].lpos;
-          if (iu < u1) issue_next(ring[s], rb[s], rc[s]);
-          fill_some(2);
-          score(kept, b, c);
+      for (int s = 0; s < kRing; ++s) {
+        if (u + s >= u1) break;
+        const int nxt = (s + kRing - 1) % kRing;  // slot of chunk u + s + kRing - 1
+        if (iu < u1) issue_next(ring[nxt], rb[nxt], rc[nxt]);
+        fill_some(2);
+        if (rb[s] != qb) {
+          load_queries(rb[s]);
+          qb = rb[s];
         }
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < kRing - 1; ++s)
-        if (iu < u1) issue_next(ring[s], rb[s], rc[s]);
-      for (int u = u0; u < u1; u += kRing) {
-#pragma unroll
-        for (int s = 0; s < kRing; ++s) {
-          if (u + s >= u1) break;
-          const int nxt = (s + kRing - 1) % kRing;  // slot of chunk u + s + kRing - 1
-          if (iu < u1) issue_next(ring[nxt], rb[nxt], rc[nxt]);
-          fill_some(2);
-          if (rb[s] != qb) {
-            load_queries(rb[s]);
-            qb = rb[s];
-          }
-          score(ring[s], rb[s], rc[s]);
-        }
+        score(ring[s], rb[s], rc[s]);
       }
     }
   };
