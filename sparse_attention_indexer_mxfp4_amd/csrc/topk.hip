@@ -398,7 +398,7 @@ __device__ __forceinline__ void finish_cached(Smem<NT> &sm, const uint32_t *keys
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t key = uint32_t(kv[e]);
-          above += int(key > top);
+          above += __popcll(__ballot(key > top));  // a wave total, counted by the scalar unit
           cm |= uint32_t((key >> 21) == d1) << (4 * j + e);
         }
       }
@@ -423,7 +423,7 @@ __device__ __forceinline__ void finish_cached(Smem<NT> &sm, const uint32_t *keys
       }
     }
   }
-  above = wave_sum(above);
+  above = uniform(above);
   match = wave_sum(match);
   if (lane == 0) {
     sm.wgt[wave] = whole_bin ? above + match : above;
@@ -532,7 +532,7 @@ __device__ __forceinline__ void finish_half(Smem<NT> &sm, uint16_t *top16, const
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t t = (uint32_t(raw[e >> 1]) >> (16 * (e & 1))) & 0xFFFFu;
-          above += int((t >> 5) > d1);
+          above += __popcll(__ballot((t >> 5) > d1));  // a wave total, counted by the scalar unit
           inbin |= uint32_t((t >> 5) == d1) << (8 * j + e);
         }
       }
@@ -553,7 +553,7 @@ __device__ __forceinline__ void finish_half(Smem<NT> &sm, uint16_t *top16, const
       }
     }
   }
-  above = wave_sum(above);
+  above = uniform(above);
   match = wave_sum(match);
   if (lane == 0) {
     sm.wgt[wave] = whole_bin ? above + match : above;
