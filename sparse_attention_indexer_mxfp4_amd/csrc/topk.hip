@@ -398,8 +398,9 @@ __device__ __forceinline__ void finish_cached(Smem<NT> &sm, const uint32_t *keys
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t key = uint32_t(kv[e]);
-          above += __popcll(__ballot(key > top));  // a wave total, counted by the scalar unit
-          cm |= uint32_t((key >> 21) == d1) << (4 * j + e);
+          const bool gt = key > top;
+          above += __popcll(__ballot(gt));  // a wave total, counted by the scalar unit
+          cm |= uint32_t(key >= (d1 << 21) && !gt) << (4 * j + e);  // key in bin d1
         }
       }
     }
@@ -516,6 +517,7 @@ __device__ __forceinline__ void finish_half(Smem<NT> &sm, uint16_t *top16, const
   const int lo = min(n, wave * seg), hi = min(n, lo + seg);
 
   const uint32_t d1 = uint32_t(sm.sel[0]);
+  const uint32_t bin_low = d1 << 5, bin_top = (d1 << 5) | 31u;  // 16-bit prefixes of bin d1
   int kr = k - sm.sel[1];
   const bool whole_bin = int(sm.hist[d1]) == kr;
   __syncthreads();  // every thread has read hist before it is cleared below
@@ -532,8 +534,10 @@ __device__ __forceinline__ void finish_half(Smem<NT> &sm, uint16_t *top16, const
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t t = (uint32_t(raw[e >> 1]) >> (16 * (e & 1))) & 0xFFFFu;
-          above += __popcll(__ballot((t >> 5) > d1));  // a wave total, counted by the scalar unit
-          inbin |= uint32_t((t >> 5) == d1) << (8 * j + e);
+          // prefixes of bin d1 are [32 d1, 32 d1 + 31]: compared whole, no field extract
+          const bool gt = t > bin_top;
+          above += __popcll(__ballot(gt));  // a wave total, counted by the scalar unit
+          inbin |= uint32_t(t >= bin_low && !gt) << (8 * j + e);
         }
       }
     }
