@@ -475,9 +475,11 @@ idx_status idx_remap_compact_topk(int32_t *topk, int64_t topk_row_stride, int32_
 #define IDX_DBG_LENGTH 1u   /* a sequence length or row bound outside its range: a
                                context length < 0, or a row end past
                                min(width, max_blocks*page_size) (the table's reach
-                               alone for the gathered walk); a row_start < 0 or a
-                               row_end < 0 or past the row's columns (idx_mqa_logits,
-                               idx_topk, idx_candidate_blocks, idx_apply_candidate_mask) */
+                               alone for the gathered walk); a row_start < 0, a
+                               row_end < 0, or a row_end past the row's columns
+                               (idx_mqa_logits, idx_topk, idx_candidate_blocks,
+                               idx_apply_candidate_mask); for idx_topk also a
+                               row_start past the width */
 #define IDX_DBG_PAGE 2u     /* a block-table entry outside [0, num_pages) read for a
                                key below its row's end */
 #define IDX_DBG_SLOT 4u     /* a slot >= 0 whose page is outside the pool (the key is
