@@ -63,7 +63,14 @@
 namespace idx {
 namespace {
 
-constexpr int kThreads = 256;
+// Threads per workgroup: 512 for single-row walks, which then hold one workgroup of
+// eight waves per CU, 256 for multi-row steps (two per CU). Measured on an MI355X
+// against 256 for everything: B = 32 decode 15.1 -> 14.9 us, MXFP4 decode 28.4 ->
+// 27.7 us, MXFP4 gathered walk 14.0 -> 12.8 us (fp8 gathered walk unchanged); the MTP
+// step lost 0.7 us with 512. Capping 256-thread workgroups at two per CU instead
+// helped the fp8 decode as much but cost the MXFP4 decode 1.4 us.
+template <int NR>
+constexpr int wg_threads() { return NR == 1 ? 512 : 256; }
 constexpr int kChunk = 64;
 constexpr int kMinChunksPerWave = 2;
 // Chunk buffers a wave holds in registers; a chunk is scored from its buffer while
@@ -173,9 +180,10 @@ constexpr int waves_per_simd() {
 // GATHER: each query row walks its own candidate pool (NR = 1, one "sequence" per
 // row); otherwise the dense walk over whole sequences, NR = next_n rows each.
 template <int FMT, int HT, int NR, bool GATHER>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<FMT, HT, NR, GATHER>())))
+__global__ __launch_bounds__(wg_threads<NR>()) __attribute__((amdgpu_waves_per_eu(waves_per_simd<FMT, HT, NR, GATHER>())))
 void paged_logits_kernel(PagedArgs a) {
   extern __shared__ int s_lds[];  // pref[S + 1], len[S] (+ end[S] for the gather walk)
+  constexpr int kThreads = wg_threads<NR>();
   __shared__ int s_scan[kThreads / 64];
   const int S = GATHER ? a.B * a.next_n : a.B;  // walks: sequences, or rows for the gather walk
   int *s_pref = s_lds;
@@ -535,14 +543,14 @@ hipError_t launch_one(const PagedArgs &a, int num_cus, size_t lds, hipStream_t s
     std::lock_guard<std::mutex> lock(mu);
     if (cached_lds != lds) {
       const hipError_t e =
-          hipOccupancyMaxActiveBlocksPerMultiprocessor(&cached, paged_logits_kernel<FMT, HT, NR, GATHER>, kThreads, lds);
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&cached, paged_logits_kernel<FMT, HT, NR, GATHER>, wg_threads<NR>(), lds);
       if (e != hipSuccess) return e;
       cached_lds = lds;
     }
     per_cu = cached;
   }
   const int nwg = max(8, (max(per_cu, 1) * num_cus) / 8 * 8);
-  paged_logits_kernel<FMT, HT, NR, GATHER><<<dim3(nwg), kThreads, lds, stream>>>(a);
+  paged_logits_kernel<FMT, HT, NR, GATHER><<<dim3(nwg), wg_threads<NR>(), lds, stream>>>(a);
   return hipGetLastError();
 }
 
