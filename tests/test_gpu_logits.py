@@ -123,6 +123,21 @@ def test_paged_page_sizes_and_heads(fmt, page_size, H):
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("H", [7, 32, 40, 128])
+def test_paged_single_row_heads(fmt, H):
+    # one row per sequence with one, two, three (of four) and eight 16-head tiles: the
+    # walk's single-row instantiations, each with its own occupancy and workgroup size
+    lens = np.array([5, 130, 700, 64, 1, 0, 1000, 257])
+    wl = workloads.paged(seed=500 + H, B=len(lens), next_n=1, H=H, ctx_lo=0, ctx_hi=0, width=1030, topk=32,
+                         fmt=fmt, context_lens=lens)
+    pi = _inputs.paged_inputs(wl, stride_pad=16)
+    got, ends = _run_paged(pi)
+    np.testing.assert_array_equal(ends, np.minimum(lens, wl.width))
+    _parity.check_logits(got, _oracle_paged(pi), _oracle_paged(pi, magnitude=True),
+                         what=f"paged {fmt} next_n=1 H={H}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
 def test_paged_per_row_lengths_and_clamping(fmt):
     lens = np.array([300, 40, 129])
     wl = workloads.paged(seed=3, B=3, next_n=2, H=64, ctx_lo=0, ctx_hi=0, width=320, topk=16, fmt=fmt,

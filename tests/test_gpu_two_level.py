@@ -143,6 +143,22 @@ def test_gather_any_list_and_page_sizes():
         np.testing.assert_array_equal(pool_end.cpu().numpy(), candidates.gather_row_ends(cand, e, block, wl.rows))
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("H", [7, 32, 40, 128])
+def test_gather_heads(fmt, H):
+    # the gathered walk's instantiations for one, two, three (of four) and eight head
+    # tiles: bit for bit the dense walk's logits at the gathered positions
+    block, n = 32, 9
+    wl, pi = _workload(fmt, 1, seed=600 + H, H=H)
+    dense, ends, bm = _source(pi, block)
+    cand = ops.idx_candidate_blocks(bm, ends, block, n)
+    pool, pool_end = ops.idx_paged_mqa_logits_gather(*_args(pi), cand, block)
+    torch.cuda.synchronize()
+    D, e, c = dense.cpu().numpy(), ends.cpu().numpy(), cand.cpu().numpy()
+    np.testing.assert_array_equal(pool.cpu().numpy(), candidates.gather_logits(D, e, c, block).astype(np.float32))
+    np.testing.assert_array_equal(pool_end.cpu().numpy(), candidates.gather_row_ends(c, e, block, wl.rows))
+
+
 @pytest.mark.parametrize("row_repeat", [1, 3])
 def test_remap(row_repeat):
     rng = np.random.default_rng(100 + row_repeat)
